@@ -1,0 +1,307 @@
+// C ABI of the draft step: argument validation (host side, before any
+// launch), workspace layout and the launch sequence on the caller's stream.
+// Declarations and the contract of every entry point: include/dflash_draft.h.
+
+#include "../../include/dflash_draft.h"
+#include "internal.hpp"
+
+#include <hip/hip_runtime.h>
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <vector>
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int ok() {
+    g_err[0] = '\0';
+    return DFLASH_OK;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+    return fail(DFLASH_EHIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+constexpr int64_t kMaxRows = 1 << 20;
+constexpr int64_t kMaxVocab = 1 << 26;
+constexpr int64_t kMaxHidden = 1 << 16;
+constexpr int64_t kMaxRank = 1 << 16;
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+int check_dims(const dflash_dims* d) {
+    if (!d) return fail(DFLASH_EINVAL, "dims is NULL");
+    if (d->num_requests < 0) return fail(DFLASH_EINVAL, "num_requests = %d < 0", d->num_requests);
+    if (d->block_len < 1 || d->block_len > DFLASH_MAX_BLOCK_LEN)
+        return fail(DFLASH_EINVAL, "block_len = %d outside [1, %d]", d->block_len, DFLASH_MAX_BLOCK_LEN);
+    if (d->total_rows < 0 || d->total_rows > kMaxRows)
+        return fail(DFLASH_EINVAL, "total_rows = %d outside [0, %lld]", d->total_rows, (long long)kMaxRows);
+    if ((int64_t)d->total_rows > (int64_t)d->num_requests * d->block_len)
+        return fail(DFLASH_EINVAL, "total_rows = %d exceeds num_requests * block_len = %lld", d->total_rows,
+                    (long long)d->num_requests * d->block_len);
+    if (d->hidden < 8 || d->hidden % 8 != 0 || d->hidden > kMaxHidden)
+        return fail(DFLASH_EINVAL, "hidden = %d must be a multiple of 8 in [8, %lld]", d->hidden,
+                    (long long)kMaxHidden);
+    if (d->draft_vocab < 1 || d->draft_vocab > kMaxVocab)
+        return fail(DFLASH_EINVAL, "draft_vocab = %d outside [1, %lld]", d->draft_vocab, (long long)kMaxVocab);
+    if (d->target_vocab < d->draft_vocab || d->target_vocab > kMaxVocab)
+        return fail(DFLASH_EINVAL, "target_vocab = %d must be in [draft_vocab = %d, %lld]", d->target_vocab,
+                    d->draft_vocab, (long long)kMaxVocab);
+    const int kmax = d->draft_vocab < DFLASH_MAX_TOP_K ? d->draft_vocab : DFLASH_MAX_TOP_K;
+    if (d->top_k < 1 || d->top_k > kmax)
+        return fail(DFLASH_EINVAL, "top_k = %d outside [1, min(64, draft_vocab) = %d]", d->top_k, kmax);
+    if (d->rank < 1 || d->rank > kMaxRank)
+        return fail(DFLASH_EINVAL, "rank = %d outside [1, %lld]", d->rank, (long long)kMaxRank);
+    if (d->walk != DFLASH_WALK_VITERBI && d->walk != DFLASH_WALK_GREEDY)
+        return fail(DFLASH_EINVAL, "walk = %d is neither DFLASH_WALK_VITERBI nor DFLASH_WALK_GREEDY", d->walk);
+    const dflash::TopkPlan p = dflash::topk_plan(d->total_rows, d->draft_vocab, d->top_k);
+    if ((int64_t)p.nchunks * d->top_k > 2048)
+        return fail(DFLASH_EUNSUPPORTED, "draft_vocab = %d is too large for top_k = %d", d->draft_vocab, d->top_k);
+    return DFLASH_OK;
+}
+
+// rows of the packed blocks: uniform blocks need M = R * L exactly
+int check_rows(const dflash_dims* d, const int32_t* row_offsets) {
+    if (!row_offsets && (int64_t)d->total_rows != (int64_t)d->num_requests * d->block_len)
+        return fail(DFLASH_EINVAL, "row_offsets is NULL but total_rows = %d != num_requests * block_len = %lld",
+                    d->total_rows, (long long)d->num_requests * d->block_len);
+    return DFLASH_OK;
+}
+
+// a required array: may be NULL only when it has no elements
+int need(const void* p, int64_t count, const char* name) {
+    if (count > 0 && !p) return fail(DFLASH_EINVAL, "%s is NULL", name);
+    return DFLASH_OK;
+}
+
+struct Layout {
+    int64_t ldz;
+    size_t logits, lse, part, best, cidx, ctok, unary, pair, total;
+    int nparts;
+};
+
+Layout layout(const dflash_dims* d) {
+    Layout l{};
+    const int64_t M = d->total_rows, K = d->top_k;
+    l.ldz = round_up(d->draft_vocab, 4);
+    l.nparts = dflash::lmhead_grid_x(d->total_rows, d->draft_vocab);
+    const dflash::TopkPlan p = dflash::topk_plan(d->total_rows, d->draft_vocab, d->top_k);
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off = (size_t)round_up((int64_t)(off + bytes), 256);
+        return at;
+    };
+    l.logits = take((size_t)(M * l.ldz) * sizeof(float));
+    l.lse = take((size_t)M * sizeof(float));
+    l.part = take((size_t)(M * l.nparts) * sizeof(float2));
+    l.best = take((size_t)(M * p.nchunks * K) * sizeof(uint64_t));
+    l.cidx = take((size_t)(M * K) * sizeof(int32_t));
+    l.ctok = take((size_t)(M * K) * sizeof(int64_t));
+    l.unary = take((size_t)(M * K) * sizeof(float));
+    l.pair = take((size_t)(M * K * K) * sizeof(float));
+    l.total = off > 0 ? off : 256;
+    return l;
+}
+
+int check_ws(const dflash_dims* d, const void* ws, size_t ws_bytes, Layout& l) {
+    l = layout(d);
+    if (!ws) return fail(DFLASH_EWORKSPACE, "workspace is NULL (%zu bytes needed)", l.total);
+    if (ws_bytes < l.total)
+        return fail(DFLASH_EWORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes needed", ws_bytes,
+                    l.total);
+    if (!aligned(ws, 256)) return fail(DFLASH_EINVAL, "workspace is not 256-byte aligned");
+    return DFLASH_OK;
+}
+
+template <class T>
+T* at(void* ws, size_t off) {
+    return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t dflash_workspace_bytes(const dflash_dims* dims) {
+    if (check_dims(dims) != DFLASH_OK) return 0;
+    ok();
+    return layout(dims).total;
+}
+
+int64_t dflash_logits_stride(int32_t draft_vocab) { return draft_vocab < 0 ? 0 : round_up(draft_vocab, 4); }
+
+int dflash_draft_block(const dflash_dims* d, const uint16_t* hidden, const uint16_t* lm_head, const int64_t* d2t,
+                       const float* tables, const float* gate_w, const int64_t* last_tok,
+                       const int32_t* row_offsets, int64_t* tokens, float* scores, void* ws, size_t ws_bytes,
+                       void* stream) {
+    int rc;
+    if ((rc = check_dims(d)) || (rc = check_rows(d, row_offsets))) return rc;
+    const int64_t M = d->total_rows, R = d->num_requests;
+    if ((rc = need(hidden, M, "hidden")) || (rc = need(lm_head, 1, "lm_head")) ||
+        (rc = need(tables, 1, "tables")) || (rc = need(last_tok, R, "last_tok")) ||
+        (rc = need(tokens, M, "tokens")) || (rc = need(scores, R, "scores")))
+        return rc;
+    if (d->target_vocab > d->draft_vocab && !d2t)
+        return fail(DFLASH_EINVAL, "target_vocab = %d > draft_vocab = %d needs d2t", d->target_vocab,
+                    d->draft_vocab);
+    if (gate_w && d2t)
+        return fail(DFLASH_EUNSUPPORTED, "gate_w with d2t: gated (DFlash v2) drafts with a pruned vocabulary are "
+                                         "not supported");
+    if (!aligned(hidden, 16) || !aligned(lm_head, 16))
+        return fail(DFLASH_EINVAL, "hidden and lm_head must be 16-byte aligned");
+    Layout l;
+    if ((rc = check_ws(d, ws, ws_bytes, l))) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    float* logits = at<float>(ws, l.logits);
+    float2* part = at<float2>(ws, l.part);
+    if ((e = dflash::launch_lmhead(hidden, lm_head, logits, l.ldz, part, d->total_rows, d->hidden,
+                                   d->draft_vocab, s)) != hipSuccess)
+        return hip_fail(e, "lm_head launch");
+    if ((e = dflash::launch_topk(logits, l.ldz, nullptr, part, l.nparts, d2t, d->total_rows, d->draft_vocab,
+                                 d->top_k, at<uint64_t>(ws, l.best), at<int32_t>(ws, l.cidx),
+                                 at<int64_t>(ws, l.ctok), at<float>(ws, l.unary), s)) != hipSuccess)
+        return hip_fail(e, "top-k launch");
+    if ((e = dflash::launch_pair_scores(at<int64_t>(ws, l.ctok), tables, gate_w, hidden, last_tok, row_offsets,
+                                        d->num_requests, d->block_len, d->total_rows, d->hidden, d->target_vocab,
+                                        d->top_k, d->rank, at<float>(ws, l.pair), s)) != hipSuccess)
+        return hip_fail(e, "pair-score launch");
+    if ((e = dflash::launch_walk(at<int64_t>(ws, l.ctok), at<float>(ws, l.unary), at<float>(ws, l.pair),
+                                 row_offsets, d->num_requests, d->block_len, d->total_rows, d->top_k, d->walk,
+                                 tokens, scores, nullptr, s)) != hipSuccess)
+        return hip_fail(e, "walk launch");
+    return ok();
+}
+
+int dflash_lm_head(const dflash_dims* d, const uint16_t* hidden, const uint16_t* lm_head, float* logits,
+                   int64_t ldz, float* lse, void* ws, size_t ws_bytes, void* stream) {
+    int rc;
+    if ((rc = check_dims(d))) return rc;
+    const int64_t M = d->total_rows;
+    if ((rc = need(hidden, M, "hidden")) || (rc = need(lm_head, 1, "lm_head")) ||
+        (rc = need(logits, M, "logits")))
+        return rc;
+    if (ldz < d->draft_vocab || ldz % 4 != 0)
+        return fail(DFLASH_EINVAL, "ldz = %lld must be >= draft_vocab = %d and a multiple of 4", (long long)ldz,
+                    d->draft_vocab);
+    if (!aligned(hidden, 16) || !aligned(lm_head, 16) || !aligned(logits, 16))
+        return fail(DFLASH_EINVAL, "hidden, lm_head and logits must be 16-byte aligned");
+    Layout l;
+    if ((rc = check_ws(d, ws, ws_bytes, l))) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    float2* part = at<float2>(ws, l.part);
+    if ((e = dflash::launch_lmhead(hidden, lm_head, logits, ldz, part, d->total_rows, d->hidden, d->draft_vocab,
+                                   s)) != hipSuccess)
+        return hip_fail(e, "lm_head launch");
+    if (lse && (e = dflash::launch_lse_combine(part, l.nparts, lse, d->total_rows, s)) != hipSuccess)
+        return hip_fail(e, "lse launch");
+    return ok();
+}
+
+int dflash_row_lse(const dflash_dims* d, const float* logits, int64_t ldz, float* lse, void* stream) {
+    int rc;
+    if ((rc = check_dims(d))) return rc;
+    const int64_t M = d->total_rows;
+    if ((rc = need(logits, M, "logits")) || (rc = need(lse, M, "lse"))) return rc;
+    if (ldz < d->draft_vocab) return fail(DFLASH_EINVAL, "ldz = %lld < draft_vocab = %d", (long long)ldz,
+                                          d->draft_vocab);
+    hipError_t e = dflash::launch_row_lse(logits, ldz, lse, d->total_rows, d->draft_vocab,
+                                          static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "row lse launch");
+    return ok();
+}
+
+int dflash_topk(const dflash_dims* d, const float* logits, int64_t ldz, const float* lse, const int64_t* d2t,
+                int32_t* cand_idx, int64_t* cand_tok, float* unary, void* ws, size_t ws_bytes, void* stream) {
+    int rc;
+    if ((rc = check_dims(d))) return rc;
+    const int64_t M = d->total_rows, MK = M * d->top_k;
+    if ((rc = need(logits, M, "logits")) || (rc = need(lse, M, "lse")) || (rc = need(cand_idx, MK, "cand_idx")) ||
+        (rc = need(cand_tok, MK, "cand_tok")) || (rc = need(unary, MK, "unary")))
+        return rc;
+    if (ldz < d->draft_vocab || ldz % 4 != 0)
+        return fail(DFLASH_EINVAL, "ldz = %lld must be >= draft_vocab = %d and a multiple of 4", (long long)ldz,
+                    d->draft_vocab);
+    if (!aligned(logits, 16)) return fail(DFLASH_EINVAL, "logits must be 16-byte aligned");
+    if (d->target_vocab > d->draft_vocab && !d2t)
+        return fail(DFLASH_EINVAL, "target_vocab = %d > draft_vocab = %d needs d2t", d->target_vocab,
+                    d->draft_vocab);
+    Layout l;
+    if ((rc = check_ws(d, ws, ws_bytes, l))) return rc;
+    hipError_t e = dflash::launch_topk(logits, ldz, lse, nullptr, 0, d2t, d->total_rows, d->draft_vocab, d->top_k,
+                                       at<uint64_t>(ws, l.best), cand_idx, cand_tok, unary,
+                                       static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "top-k launch");
+    return ok();
+}
+
+int dflash_pair_scores(const dflash_dims* d, const int64_t* cand_tok, const float* tables, const float* gate_w,
+                       const uint16_t* hidden, const int64_t* last_tok, const int32_t* row_offsets, float* pair,
+                       void* stream) {
+    int rc;
+    if ((rc = check_dims(d)) || (rc = check_rows(d, row_offsets))) return rc;
+    const int64_t M = d->total_rows, R = d->num_requests;
+    if ((rc = need(cand_tok, M, "cand_tok")) || (rc = need(tables, 1, "tables")) ||
+        (rc = need(last_tok, R, "last_tok")) || (rc = need(pair, M, "pair")))
+        return rc;
+    if (gate_w && (rc = need(hidden, M, "hidden (read by the gate)"))) return rc;
+    hipError_t e = dflash::launch_pair_scores(cand_tok, tables, gate_w, hidden, last_tok, row_offsets,
+                                              d->num_requests, d->block_len, d->total_rows, d->hidden,
+                                              d->target_vocab, d->top_k, d->rank, pair,
+                                              static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "pair-score launch");
+    return ok();
+}
+
+int dflash_walk(const dflash_dims* d, const int64_t* cand_tok, const float* unary, const float* pair,
+                const int32_t* row_offsets, int64_t* tokens, float* scores, int32_t* slots, void* stream) {
+    int rc;
+    if ((rc = check_dims(d)) || (rc = check_rows(d, row_offsets))) return rc;
+    const int64_t M = d->total_rows, R = d->num_requests;
+    if ((rc = need(cand_tok, M, "cand_tok")) || (rc = need(unary, M, "unary")) || (rc = need(pair, M, "pair")) ||
+        (rc = need(tokens, M, "tokens")) || (rc = need(scores, R, "scores")))
+        return rc;
+    hipError_t e = dflash::launch_walk(cand_tok, unary, pair, row_offsets, d->num_requests, d->block_len,
+                                       d->total_rows, d->top_k, d->walk, tokens, scores, slots,
+                                       static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "walk launch");
+    return ok();
+}
+
+int dflash_check_d2t(const int64_t* d2t, int32_t Vd, int32_t Vt, int* is_injective) {
+    if (!d2t) return fail(DFLASH_EINVAL, "d2t is NULL");
+    if (!is_injective) return fail(DFLASH_EINVAL, "is_injective is NULL");
+    if (Vd < 1 || Vt < Vd) return fail(DFLASH_EINVAL, "need 1 <= draft_vocab = %d <= target_vocab = %d", Vd, Vt);
+    std::vector<uint8_t> seen((size_t)Vt, 0);
+    int inj = 1;
+    for (int32_t i = 0; i < Vd; ++i) {
+        const int64_t t = (int64_t)i + d2t[i];
+        if (t < 0 || t >= Vt)
+            return fail(DFLASH_EINVAL, "d2t[%d] = %lld maps draft token %d to %lld, outside [0, %d)", i,
+                        (long long)d2t[i], i, (long long)t, Vt);
+        if (seen[(size_t)t]) inj = 0;
+        seen[(size_t)t] = 1;
+    }
+    *is_injective = inj;
+    return ok();
+}
+
+const char* dflash_last_error(void) { return g_err; }
+
+}  // extern "C"

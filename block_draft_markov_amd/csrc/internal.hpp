@@ -1,0 +1,42 @@
+// Internal launch interface between the C ABI (abi.hip) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dflash {
+
+// ---------------------------------------------------------------- part 1: lm_head GEMM
+// Vocabulary rows are handled in tiles of 16; a workgroup owns a contiguous
+// range of tiles and keeps one (max, sum exp) partial per row.
+int lmhead_grid_x(int M, int V);          // workgroups along the vocabulary
+int lmhead_grid_y(int M);                 // workgroups along the rows
+hipError_t launch_lmhead(const uint16_t* hidden, const uint16_t* W, float* logits, int64_t ldz,
+                         float2* lse_part, int M, int H, int V, hipStream_t s);
+// lse[m] from the partials of row m.
+hipError_t launch_lse_combine(const float2* lse_part, int nparts, float* lse, int M, hipStream_t s);
+// lse[m] straight from logits.
+hipError_t launch_row_lse(const float* logits, int64_t ldz, float* lse, int M, int V, hipStream_t s);
+
+// ---------------------------------------------------------------- part 2: Top-K
+struct TopkPlan {
+    int per_thread;   // logits per thread in a chunk (16, 32 or 64)
+    int chunk;        // logits per chunk = 256 * per_thread
+    int nchunks;      // chunks per row
+};
+TopkPlan topk_plan(int M, int V, int K);
+hipError_t launch_topk(const float* logits, int64_t ldz, const float* lse, const float2* lse_part,
+                       int nparts, const int64_t* d2t, int M, int V, int K, uint64_t* chunk_best,
+                       int32_t* cand_idx, int64_t* cand_tok, float* unary, hipStream_t s);
+
+// ---------------------------------------------------------------- parts 3 and 4: lattice
+hipError_t launch_pair_scores(const int64_t* cand_tok, const float* tables, const float* gate_w,
+                              const uint16_t* hidden, const int64_t* last_tok,
+                              const int32_t* row_offsets, int R, int L, int M, int H, int Vt,
+                              int K, int r, float* pair, hipStream_t s);
+hipError_t launch_walk(const int64_t* cand_tok, const float* unary, const float* pair,
+                       const int32_t* row_offsets, int R, int L, int M, int K, int walk,
+                       int64_t* tokens, float* scores, int32_t* slots, hipStream_t s);
+
+}  // namespace dflash

@@ -1,0 +1,331 @@
+// Part 2 of the draft step: the K = min(64, V_d) best draft tokens of every
+// row in slot order (logit descending, draft id ascending), the d2t remap of
+// draft token i to target token i + d2t[i], and the unary score z - lse
+// (optimum-intel page "Support MiniCPM-OCR-1.0-DSpark", What does this PR
+// do?; the Markov head needs "the radix TopK" on the GPU per the page "Export
+// DFlash v2 and DSpark drafts ...", What does this PR do?; ties ordered by
+// index as in the TopP commit of the openvino.genai page).
+//
+// Stage 1 (topk_chunk): a grid of (chunk, row) workgroups; a chunk is 256
+// threads x PT logits held in registers, read from HBM once with 16-byte
+// loads.  Every logit becomes an order-preserving uint32 key.  If tau is the
+// K-th largest of the 256 per-thread maxima, at least K keys of the chunk are
+// >= tau, so every member of the chunk's top K is >= tau: only those
+// survivors (about K + 10 for smooth rows) are ranked, each by counting the
+// survivors that beat it, which yields the slot order directly.  When more
+// than 256 keys survive (heavy ties), an exact radix select on 8-bit digits
+// finds the K-th key instead, and equal keys are taken in id order.
+// Stage 2 (topk_merge): one workgroup per row merges the sorted per-chunk
+// lists pairwise in LDS (each entry's merged position = its own index + the
+// number of entries of the other list that beat it, by binary search), then
+// writes ids, target ids and unary scores.
+// Entries are (key << 32 | ~id), so a larger entry is the better slot and
+// every comparison is one 64-bit compare.
+
+#include "common.hpp"
+#include "internal.hpp"
+
+#include <math.h>
+
+namespace dflash {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kFastCap = 256;   // survivors ranked directly
+
+__device__ __forceinline__ int block_excl_scan(int v, int* wsum, int& total) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    int x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+    }
+    if (lane == 63) wsum[w] = x;
+    __syncthreads();
+    int off = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int s = wsum[i];
+        off += (i < w) ? s : 0;
+        tot += s;
+    }
+    __syncthreads();
+    total = tot;
+    return off + x - v;
+}
+
+// Slot-order the n unique entries of list[0..n) and write the first K to out
+// (empty entries fill the rest when n < K).
+__device__ __forceinline__ void rank_place(const uint64_t* list, int n, int K, uint64_t* out) {
+    for (int i = threadIdx.x; i < n; i += kThreads) {
+        const uint64_t my = list[i];
+        int rank = 0;
+        for (int j = 0; j < n; ++j) rank += (list[j] > my) ? 1 : 0;
+        if (rank < K) out[rank] = my;
+    }
+    for (int i = n + threadIdx.x; i < K; i += kThreads) out[i] = kEmptyEntry;
+}
+
+template <int PT>
+__global__ void __launch_bounds__(kThreads) topk_chunk_kernel(const float* __restrict__ logits, int64_t ldz,
+                                                              int V, int K, int nchunks,
+                                                              uint64_t* __restrict__ best) {
+    __shared__ uint32_t tmax[kThreads];
+    __shared__ uint64_t cand[kFastCap];
+    __shared__ uint32_t hist[256];
+    __shared__ int wsum[4];
+    __shared__ uint32_t s_tau;
+    __shared__ int s_digit, s_want;
+
+    const int tid = threadIdx.x;
+    const int c = blockIdx.x, m = blockIdx.y;
+    const int cbase = c * (kThreads * PT);
+    const float* row = logits + (int64_t)m * ldz;
+    uint64_t* out = best + ((int64_t)m * nchunks + c) * K;
+
+    // ---- load PT logits per thread: element (j, q) has id cbase + j*1024 + 4*tid + q
+    uint32_t key[PT];
+#pragma unroll
+    for (int j = 0; j < PT / 4; ++j) {
+        const int v = cbase + j * (4 * kThreads) + 4 * tid;
+        f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        if (v < V) z = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + v));
+#pragma unroll
+        for (int q = 0; q < 4; ++q) key[4 * j + q] = (v + q < V) ? float_to_key(z[q]) : 0u;
+    }
+    auto id_of = [&](int e) { return (uint32_t)(cbase + (e >> 2) * (4 * kThreads) + 4 * tid + (e & 3)); };
+
+    // ---- tau: K-th largest per-thread maximum (ties ranked by thread index)
+    uint32_t mx = 0;
+#pragma unroll
+    for (int e = 0; e < PT; ++e) mx = max(mx, key[e]);
+    tmax[tid] = mx;
+    __syncthreads();
+    {
+        int rank = 0;
+        for (int i = 0; i < kThreads; ++i) {
+            const uint32_t o = tmax[i];
+            rank += (o > mx || (o == mx && i < tid)) ? 1 : 0;
+        }
+        if (rank == K - 1) s_tau = mx;
+    }
+    __syncthreads();
+    const uint32_t tau = max(s_tau, 1u);   // key 0 marks positions past the row
+
+    int cnt = 0;
+#pragma unroll
+    for (int e = 0; e < PT; ++e) cnt += (key[e] >= tau) ? 1 : 0;
+    int n;
+    const int pos = block_excl_scan(cnt, wsum, n);
+
+    if (n <= kFastCap) {
+        int p = pos;
+#pragma unroll
+        for (int e = 0; e < PT; ++e)
+            if (key[e] >= tau && p < kFastCap) cand[p++] = pack_entry(key[e], id_of(e));
+        __syncthreads();
+        rank_place(cand, n, K, out);
+        return;
+    }
+
+    // ---- fallback: exact K-th key by radix select on 8-bit digits
+    if (tid == 0) { s_digit = 0; s_want = 1; }
+    uint32_t prefix = 0, pmask = 0;
+    int want = K;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+        hist[tid] = 0;
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < PT; ++e)
+            if (key[e] != 0u && (key[e] & pmask) == prefix) atomicAdd(&hist[(key[e] >> shift) & 255u], 1u);
+        __syncthreads();
+        if (tid == 0) {
+            int cum = 0;
+            for (int d = 255; d >= 0; --d) {
+                const int h = (int)hist[d];
+                if (cum + h >= want) { s_digit = d; s_want = want - cum; break; }
+                cum += h;
+            }
+        }
+        __syncthreads();
+        prefix |= (uint32_t)s_digit << shift;
+        pmask |= 255u << shift;
+        want = s_want;
+        __syncthreads();
+    }
+    const uint32_t T = prefix;   // the K-th largest key; `want` keys equal to T are taken
+    int ngt_t = 0;
+#pragma unroll
+    for (int e = 0; e < PT; ++e) ngt_t += (key[e] > T) ? 1 : 0;
+    int ngt;
+    int p = block_excl_scan(ngt_t, wsum, ngt);
+#pragma unroll
+    for (int e = 0; e < PT; ++e)
+        if (key[e] > T && p < K) cand[p++] = pack_entry(key[e], id_of(e));
+    // equal keys in id order: id order is (j, thread, q)
+    int taken_base = 0;
+#pragma unroll
+    for (int j = 0; j < PT / 4; ++j) {
+        int neq = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) neq += (key[4 * j + q] == T) ? 1 : 0;
+        int tot;
+        int ord = taken_base + block_excl_scan(neq, wsum, tot);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if (key[4 * j + q] == T) {
+                if (ord < want && ngt + ord < K) cand[ngt + ord] = pack_entry(T, id_of(4 * j + q));
+                ++ord;
+            }
+        }
+        taken_base += tot;
+    }
+    __syncthreads();
+    rank_place(cand, K, K, out);
+}
+
+// Number of entries of the descending list y[0..n) that are > x (strict) or
+// >= x (when `or_equal`).
+__device__ __forceinline__ int count_better(const uint64_t* y, int n, uint64_t x, bool or_equal) {
+    int lo = 0, hi = n;   // first index whose entry does not beat x
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        const bool beats = or_equal ? (y[mid] >= x) : (y[mid] > x);
+        if (beats) lo = mid + 1; else hi = mid;
+    }
+    return lo;
+}
+
+__device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
+    if (s2 == 0.f) return;
+    if (s == 0.f) { m = m2; s = s2; return; }
+    const float mn = fmaxf(m, m2);
+    s = s * expf(m - mn) + s2 * expf(m2 - mn);
+    m = mn;
+}
+
+__global__ void __launch_bounds__(kThreads) topk_merge_kernel(const uint64_t* __restrict__ best, int nchunks, int K,
+                                                              const float* __restrict__ lse_in,
+                                                              const float2* __restrict__ lse_part, int nparts,
+                                                              const int64_t* __restrict__ d2t, int V,
+                                                              int32_t* __restrict__ cand_idx,
+                                                              int64_t* __restrict__ cand_tok,
+                                                              float* __restrict__ unary) {
+    extern __shared__ uint64_t lists[];   // 2 * nchunks * K entries
+    __shared__ float s_lse;
+    const int tid = threadIdx.x;
+    const int m = blockIdx.x;
+    uint64_t* a = lists;
+    uint64_t* b = lists + (int64_t)nchunks * K;
+    const uint64_t* src = best + (int64_t)m * nchunks * K;
+    for (int i = tid; i < nchunks * K; i += kThreads) a[i] = src[i];
+
+    if (tid < 64) {
+        float lse;
+        if (lse_part) {
+            float mx = 0.f, sm = 0.f;
+            for (int i = tid; i < nparts; i += 64) {
+                const float2 pp = lse_part[(int64_t)m * nparts + i];
+                lse_merge(mx, sm, pp.x, pp.y);
+            }
+            for (int o = 32; o > 0; o >>= 1) {
+                const float m2 = __shfl_xor(mx, o);
+                const float s2 = __shfl_xor(sm, o);
+                lse_merge(mx, sm, m2, s2);
+            }
+            lse = mx + logf(sm);
+        } else {
+            lse = lse_in[m];
+        }
+        if (tid == 0) s_lse = lse;
+    }
+    __syncthreads();
+
+    int nl = nchunks;
+    while (nl > 1) {
+        const int pairs = nl >> 1;
+        // one thread per entry of both lists of every pair
+        for (int i = tid; i < pairs * 2 * K; i += kThreads) {
+            const int pr = i / (2 * K), r = i % (2 * K);
+            const uint64_t* x = a + (int64_t)(2 * pr) * K;
+            const uint64_t* y = x + K;
+            int dst;
+            uint64_t e;
+            if (r < K) { e = x[r]; dst = r + count_better(y, K, e, false); }
+            else { e = y[r - K]; dst = (r - K) + count_better(x, K, e, true); }
+            if (dst < K) b[(int64_t)pr * K + dst] = e;
+        }
+        if (nl & 1)
+            for (int i = tid; i < K; i += kThreads) b[(int64_t)pairs * K + i] = a[(int64_t)(nl - 1) * K + i];
+        __syncthreads();
+        uint64_t* t = a; a = b; b = t;
+        nl = pairs + (nl & 1);
+    }
+
+    const float lse = s_lse;
+    for (int k = tid; k < K; k += kThreads) {
+        const uint64_t e = a[k];
+        uint32_t id = entry_id(e);
+        id = min(id, (uint32_t)(V - 1));   // an empty entry cannot reach the top K when K <= V
+        const float z = key_to_float(entry_key(e));
+        const int64_t o = (int64_t)m * K + k;
+        cand_idx[o] = (int32_t)id;
+        cand_tok[o] = d2t ? (int64_t)id + d2t[id] : (int64_t)id;
+        unary[o] = z - lse;
+    }
+}
+
+template <int PT>
+hipError_t launch_chunks(const float* logits, int64_t ldz, int V, int K, int M, int nchunks, uint64_t* best,
+                         hipStream_t s) {
+    hipLaunchKernelGGL((topk_chunk_kernel<PT>), dim3(nchunks, M), dim3(kThreads), 0, s, logits, ldz, V, K,
+                       nchunks, best);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+TopkPlan topk_plan(int M, int V, int K) {
+    // The largest chunk that still gives about four workgroups per CU, as long
+    // as the per-row merge holds at most 2048 entries (2 x 16 KB of LDS).
+    TopkPlan p{16, 256 * 16, 0};
+    const int pts[3] = {64, 32, 16};
+    for (int i = 0; i < 3; ++i) {
+        const int chunk = 256 * pts[i];
+        const int nc = (V + chunk - 1) / chunk;
+        if ((int64_t)M * nc >= 1024 || pts[i] == 16) {
+            p.per_thread = pts[i];
+            p.chunk = chunk;
+            p.nchunks = nc;
+            break;
+        }
+    }
+    while ((int64_t)p.nchunks * K > 2048 && p.per_thread < 64) {
+        p.per_thread *= 2;
+        p.chunk = 256 * p.per_thread;
+        p.nchunks = (V + p.chunk - 1) / p.chunk;
+    }
+    return p;
+}
+
+hipError_t launch_topk(const float* logits, int64_t ldz, const float* lse, const float2* lse_part, int nparts,
+                       const int64_t* d2t, int M, int V, int K, uint64_t* chunk_best, int32_t* cand_idx,
+                       int64_t* cand_tok, float* unary, hipStream_t s) {
+    if (M <= 0) return hipSuccess;
+    const TopkPlan p = topk_plan(M, V, K);
+    hipError_t e;
+    switch (p.per_thread) {
+        case 64: e = launch_chunks<64>(logits, ldz, V, K, M, p.nchunks, chunk_best, s); break;
+        case 32: e = launch_chunks<32>(logits, ldz, V, K, M, p.nchunks, chunk_best, s); break;
+        default: e = launch_chunks<16>(logits, ldz, V, K, M, p.nchunks, chunk_best, s); break;
+    }
+    if (e != hipSuccess) return e;
+    const size_t lds = (size_t)2 * p.nchunks * K * sizeof(uint64_t);
+    hipLaunchKernelGGL(topk_merge_kernel, dim3(M), dim3(kThreads), lds, s, chunk_best, p.nchunks, K, lse,
+                       lse_part, nparts, d2t, V, cand_idx, cand_tok, unary);
+    return hipGetLastError();
+}
+
+}  // namespace dflash

@@ -1,0 +1,177 @@
+/*
+ * dflash_draft.h — C ABI of the DFlash/DSpark draft step on MI355X (gfx950).
+ *
+ * The draft step turns the hidden states of the packed block rows of all
+ * scheduled requests into drafted tokens, in four parts:
+ *   1. lm_head projection to logits over the draft vocabulary
+ *      (optimum-intel page "Support MiniCPM-OCR-1.0-DSpark", What does this
+ *      PR do?: the draft applies its own lm_head over the draft vocabulary);
+ *   2. Top-K per row, K = min(64, draft vocabulary), with the d2t remap of
+ *      draft token i to target token i + d2t[i] (same page and section);
+ *   3. the Markov-head candidate scorer over the K x K transitions between
+ *      neighbouring positions, gated by the draft hidden states for DFlash v2
+ *      (optimum-intel page "Export DFlash v2 and DSpark drafts ...", What does
+ *      this PR do?; openvino.genai page "Add DSpark and DFlash v2 drafts ...",
+ *      commit "DFlash-2 Markov head / BlockRowSource");
+ *   4. a walk through that lattice for every request in one launch: the
+ *      max-score path, or the greedy walk taking the best candidate after the
+ *      token before (openvino.genai page, same commit).
+ *
+ * Scoring (the pages fix none; this is the definition the library computes):
+ *   z_m[v]    = sum_i W[v,i] h_m[i]                (bf16 inputs, fp32 accumulation)
+ *   lse_m     = log sum_v exp z_m[v]               (over the draft vocabulary)
+ *   slots     = the K largest z_m, ordered by (z descending, draft id ascending)
+ *   t_m[k]    = cand_m[k] + d2t[cand_m[k]]         (cand_m[k] when d2t is NULL)
+ *   u_m[k]    = z_m[cand_m[k]] - lse_m
+ *   g_m       = 1 / (1 + exp(-w . h_m)) when gate_w is given, else 1
+ *   S_p[j][k] = g_m(p) * <A[t_{m(p-1)}[j]], B[t_{m(p)}[k]]>  for p >= 1,
+ *   S_0[0][k] = g_m(0) * <A[last_tok], B[t_{m(0)}[k]]>
+ *   Score(c)  = sum_p u_{m(p)}[c_p] + S_p[c_{p-1}][c_p]
+ *   Viterbi: the max-Score path; at every max the lowest slot wins.
+ *   Greedy:  c_p = lowest argmax_k u_{m(p)}[k] + S_p[c_{p-1}][k].
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer is caller-owned DEVICE memory unless stated otherwise.
+ *     The library allocates nothing, keeps no state between calls and is
+ *     re-entrant; all work is enqueued on `stream` (a hipStream_t; NULL is
+ *     the null stream) and outputs are valid once the caller has
+ *     synchronised with that stream.
+ *   - bf16 tensors are passed as uint16_t bit patterns.
+ *   - Inputs must not alias outputs or the workspace.
+ *   - Return value: DFLASH_OK (0) or a negative DFLASH_E* code.  On any error
+ *     nothing is launched and no output is written; dflash_last_error()
+ *     names the offending argument.  Argument checks are host-side and
+ *     happen before any launch.
+ *   - Device-data preconditions that the host cannot see (token ids in
+ *     range, 0 <= i + d2t[i] < V_t, row_offsets well formed) are the caller's;
+ *     dflash_check_d2t() checks d2t once on the host.  Kernels clamp every
+ *     index they read so that a broken precondition gives wrong tokens, never
+ *     an out-of-bounds access.
+ *   - Inputs must be finite; NaN or Inf logits give unspecified tokens.
+ */
+#ifndef DFLASH_DRAFT_H
+#define DFLASH_DRAFT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DFLASH_OK            0
+#define DFLASH_EINVAL       -1  /* a bad size, a NULL required pointer, a bad mode */
+#define DFLASH_EUNSUPPORTED -2  /* a legal but unsupported combination */
+#define DFLASH_EWORKSPACE   -3  /* workspace NULL or smaller than dflash_workspace_bytes() */
+#define DFLASH_EHIP         -4  /* the HIP runtime reported an error (message in dflash_last_error) */
+
+#define DFLASH_WALK_VITERBI  0  /* max-score path over all K^L paths */
+#define DFLASH_WALK_GREEDY   1  /* best candidate after the token before, position by position */
+
+#define DFLASH_MAX_TOP_K     64
+/* A block is at most num_assistant_tokens rows, which GenerationConfig
+ * validation caps at 100 (openvino.genai page, the docs commit on the
+ * num_assistant_tokens limit). */
+#define DFLASH_MAX_BLOCK_LEN 100
+
+/* Sizes of one call.  M = total_rows packed block rows; without row_offsets
+ * every request owns block_len consecutive rows and total_rows must equal
+ * num_requests * block_len; with row_offsets request r owns rows
+ * row_offsets[r] .. row_offsets[r+1]-1, each at most block_len of them. */
+typedef struct dflash_dims {
+    int32_t num_requests;  /* R >= 0 */
+    int32_t block_len;     /* L in [1, 100]: rows per request (the maximum with row_offsets) */
+    int32_t total_rows;    /* M >= 0 */
+    int32_t hidden;        /* H >= 8, a multiple of 8 */
+    int32_t draft_vocab;   /* V_d >= 1 */
+    int32_t target_vocab;  /* V_t >= V_d; V_t > V_d needs d2t */
+    int32_t top_k;         /* K in [1, min(64, V_d)] */
+    int32_t rank;          /* r >= 1, table rank */
+    int32_t walk;          /* DFLASH_WALK_VITERBI or DFLASH_WALK_GREEDY */
+} dflash_dims;
+
+/* Bytes of workspace every entry point below needs for these dims (the same
+ * number for all of them), or 0 with dflash_last_error() set if the dims are
+ * invalid.  The workspace must be device memory aligned to 256 bytes. */
+size_t dflash_workspace_bytes(const dflash_dims* dims);
+
+/* Row stride, in floats, of the logits buffers the stage entry points take:
+ * draft_vocab rounded up to a multiple of 4 (16-byte aligned rows). */
+int64_t dflash_logits_stride(int32_t draft_vocab);
+
+/* The whole draft step (parts 1-4) in one call.
+ *   hidden      bf16 [M][H] row-major: draft hidden states of the packed block rows
+ *   lm_head     bf16 [V_d][H] row-major (nn.Linear layout): the draft lm_head
+ *   d2t         int64 [V_d] or NULL: target id of draft token i is i + d2t[i]
+ *   tables      fp32 [2][V_t][r]: tables[0] = A (indexed by the previous token),
+ *               tables[1] = B (indexed by the candidate token)
+ *   gate_w      fp32 [H] or NULL: gated (DFlash v2) transitions when given
+ *   last_tok    int64 [R]: the last accepted target token of every request
+ *   row_offsets int32 [R+1] or NULL (uniform blocks of block_len rows)
+ *   tokens      out int64 [M]: drafted target token of every row
+ *   scores      out fp32 [R]: Score of the chosen path (0 for a request without rows)
+ *   workspace   device scratch of dflash_workspace_bytes(dims) bytes
+ * gate_w together with d2t returns DFLASH_EUNSUPPORTED: DFlash v2 drafts with a
+ * pruned vocabulary are rejected (optimum-intel page "Support
+ * MiniCPM-OCR-1.0-DSpark", What does this PR do?). */
+int dflash_draft_block(const dflash_dims* dims,
+                       const uint16_t* hidden, const uint16_t* lm_head,
+                       const int64_t* d2t, const float* tables, const float* gate_w,
+                       const int64_t* last_tok, const int32_t* row_offsets,
+                       int64_t* tokens, float* scores,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Part 1: logits[m][v] (fp32, row stride ldz >= V_d, ldz % 4 == 0) of every row
+ * and lse[m] (fp32 [M], or NULL to skip it), from bf16 hidden [M][H] and
+ * lm_head [V_d][H].  The per-row (max, sum exp) partials stay in the workspace. */
+int dflash_lm_head(const dflash_dims* dims, const uint16_t* hidden, const uint16_t* lm_head,
+                   float* logits, int64_t ldz, float* lse,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* lse[m] = log sum_v exp logits[m][v] over the first V_d entries of every row
+ * (row stride ldz), for logits that did not come from dflash_lm_head. */
+int dflash_row_lse(const dflash_dims* dims, const float* logits, int64_t ldz, float* lse,
+                   void* stream);
+
+/* Part 2: the K slots of every row in slot order.
+ *   logits fp32 [M][ldz], lse fp32 [M], d2t int64 [V_d] or NULL
+ *   cand_idx out int32 [M][K] draft ids; cand_tok out int64 [M][K] target ids;
+ *   unary out fp32 [M][K] = z - lse. */
+int dflash_topk(const dflash_dims* dims, const float* logits, int64_t ldz, const float* lse,
+                const int64_t* d2t, int32_t* cand_idx, int64_t* cand_tok, float* unary,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Part 3: transition scores of every row, out fp32 pair [M][K][K]:
+ * pair[m(p)][j][k] = S_p[j][k] for p >= 1; for p = 0 row j = 0 holds S_0[0][k]
+ * and rows j >= 1 are written as 0.
+ *   cand_tok int64 [M][K], tables fp32 [2][V_t][r], gate_w fp32 [H] or NULL,
+ *   hidden bf16 [M][H] (read only when gate_w is given), last_tok int64 [R],
+ *   row_offsets int32 [R+1] or NULL. */
+int dflash_pair_scores(const dflash_dims* dims, const int64_t* cand_tok, const float* tables,
+                       const float* gate_w, const uint16_t* hidden, const int64_t* last_tok,
+                       const int32_t* row_offsets, float* pair, void* stream);
+
+/* Part 4: the walk of every request over unary fp32 [M][K] and pair fp32
+ * [M][K][K] (as written by dflash_pair_scores), one launch for all requests.
+ *   tokens out int64 [M] = cand_tok[m][c_p]; scores out fp32 [R];
+ *   slots out int32 [M] (the chosen slot c_p of every row) or NULL. */
+int dflash_walk(const dflash_dims* dims, const int64_t* cand_tok, const float* unary,
+                const float* pair, const int32_t* row_offsets,
+                int64_t* tokens, float* scores, int32_t* slots, void* stream);
+
+/* HOST memory: checks once, at set-up, that every i + d2t[i] lies in
+ * [0, V_t) (returns DFLASH_EINVAL naming the first bad i otherwise) and
+ * writes 1 to *is_injective when no two draft ids share a target id, else 0
+ * (openvino.genai page, d2t commit: the size is checked per call, injectivity
+ * once; greedy drafting accepts any mapping). */
+int dflash_check_d2t(const int64_t* d2t_host, int32_t draft_vocab, int32_t target_vocab,
+                     int* is_injective);
+
+/* Message of the last error on the calling thread ("" after success). */
+const char* dflash_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DFLASH_DRAFT_H */

@@ -1,0 +1,180 @@
+"""The C ABI on the CPU: the library loads, exports every symbol that
+include/*.h declares, and rejects bad arguments on the host before any launch
+(no GPU is touched: every call here fails validation first)."""
+import ctypes
+import glob
+import os
+import re
+
+import numpy as np
+import pytest
+
+import block_draft_markov_amd as bdm
+from block_draft_markov_amd._lib import Dims
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x100000          # a 256-byte aligned non-NULL address; never dereferenced (validation fails first)
+FAKE_ODD = 0x100008      # 8-byte aligned only
+
+
+def header_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"\b(dflash_\w+)\s*\(", text))
+    return sorted(names)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return bdm.load()
+
+
+def dims(**kw):
+    base = dict(num_requests=2, block_len=3, total_rows=6, hidden=64, draft_vocab=1024, target_vocab=1024,
+                top_k=8, rank=16, walk=0)
+    base.update(kw)
+    return Dims(**base)
+
+
+def err(lib):
+    return lib.dflash_last_error().decode()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = header_functions()
+    assert len(names) == 10, names
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in include/ but not exported"
+    assert set(names) == set(bdm.SIGNATURES), "binding and header disagree"
+
+
+def test_workspace_bytes_and_stride(lib):
+    d = dims()
+    n = lib.dflash_workspace_bytes(ctypes.byref(d))
+    assert n > 0 and n % 256 == 0
+    # grows with the rows and the vocabulary
+    assert lib.dflash_workspace_bytes(ctypes.byref(dims(num_requests=4, total_rows=12))) > n
+    assert lib.dflash_workspace_bytes(ctypes.byref(dims(draft_vocab=4096, target_vocab=4096))) > n
+    assert lib.dflash_logits_stride(151936) == 151936
+    assert lib.dflash_logits_stride(1023) == 1024
+    assert lib.dflash_logits_stride(48) == 48
+    # invalid dims -> 0 and a message
+    assert lib.dflash_workspace_bytes(ctypes.byref(dims(top_k=0))) == 0
+    assert "top_k" in err(lib)
+    assert lib.dflash_workspace_bytes(None) == 0
+
+
+@pytest.mark.parametrize("kw,code,word", [
+    (dict(top_k=0), bdm.EINVAL, "top_k"),
+    (dict(top_k=65, draft_vocab=100000, target_vocab=100000), bdm.EINVAL, "top_k"),
+    (dict(top_k=49, draft_vocab=48, target_vocab=48), bdm.EINVAL, "top_k"),   # K <= min(64, V_d)
+    (dict(block_len=0, total_rows=0), bdm.EINVAL, "block_len"),
+    (dict(block_len=101, total_rows=202), bdm.EINVAL, "block_len"),
+    (dict(hidden=60), bdm.EINVAL, "hidden"),
+    (dict(hidden=0), bdm.EINVAL, "hidden"),
+    (dict(draft_vocab=0), bdm.EINVAL, "draft_vocab"),
+    (dict(target_vocab=1000), bdm.EINVAL, "target_vocab"),
+    (dict(rank=0), bdm.EINVAL, "rank"),
+    (dict(walk=2), bdm.EINVAL, "walk"),
+    (dict(num_requests=-1), bdm.EINVAL, "num_requests"),
+    (dict(total_rows=7), bdm.EINVAL, "total_rows"),
+    (dict(total_rows=5), bdm.EINVAL, "row_offsets"),   # uniform blocks need M = R * L
+])
+def test_draft_block_rejects_bad_dims(lib, kw, code, word):
+    d = dims(**kw)
+    rc = lib.dflash_draft_block(ctypes.byref(d), FAKE, FAKE, None, FAKE, None, FAKE, None, FAKE, FAKE, FAKE,
+                                1 << 40, None)
+    assert rc == code
+    assert word in err(lib)
+
+
+def test_draft_block_pointer_and_mode_rules(lib):
+    d = dims()
+    big = 1 << 40
+    call = lambda **p: lib.dflash_draft_block(
+        ctypes.byref(p.get("d", d)), p.get("hidden", FAKE), p.get("lm", FAKE), p.get("d2t", None),
+        p.get("tables", FAKE), p.get("gate", None), p.get("last", FAKE), p.get("off", None), p.get("tok", FAKE),
+        p.get("sc", FAKE), p.get("ws", FAKE), p.get("wsn", big), None)
+    assert call(hidden=None) == bdm.EINVAL and "hidden" in err(lib)
+    assert call(lm=None) == bdm.EINVAL and "lm_head" in err(lib)
+    assert call(tables=None) == bdm.EINVAL and "tables" in err(lib)
+    assert call(last=None) == bdm.EINVAL and "last_tok" in err(lib)
+    assert call(tok=None) == bdm.EINVAL and "tokens" in err(lib)
+    assert call(sc=None) == bdm.EINVAL and "scores" in err(lib)
+    # a pruned vocabulary needs d2t
+    dp = dims(target_vocab=4096)
+    assert call(d=dp) == bdm.EINVAL and "d2t" in err(lib)
+    # gated transitions with a pruned vocabulary are rejected
+    assert call(d=dp, d2t=FAKE, gate=FAKE) == bdm.EUNSUPPORTED and "gate_w" in err(lib)
+    # workspace
+    assert call(ws=None) == bdm.EWORKSPACE
+    need = lib.dflash_workspace_bytes(ctypes.byref(d))
+    assert call(wsn=need - 1) == bdm.EWORKSPACE and str(need) in err(lib)
+    assert call(ws=FAKE_ODD) == bdm.EINVAL and "aligned" in err(lib)
+    # 16-byte alignment of the bf16 operands
+    assert call(hidden=FAKE + 2) == bdm.EINVAL and "aligned" in err(lib)
+
+
+def test_stage_entry_points_validate(lib):
+    d = dims()
+    big = 1 << 40
+    # lm_head: ldz must cover V_d and be a multiple of 4
+    assert lib.dflash_lm_head(ctypes.byref(d), FAKE, FAKE, FAKE, 1022, FAKE, FAKE, big, None) == bdm.EINVAL
+    assert "ldz" in err(lib)
+    assert lib.dflash_lm_head(ctypes.byref(d), FAKE, FAKE, FAKE, 1026, FAKE, FAKE, big, None) == bdm.EINVAL
+    assert lib.dflash_lm_head(ctypes.byref(d), FAKE, FAKE, None, 1024, FAKE, FAKE, big, None) == bdm.EINVAL
+    assert "logits" in err(lib)
+    assert lib.dflash_row_lse(ctypes.byref(d), FAKE, 1000, FAKE, None) == bdm.EINVAL
+    assert lib.dflash_row_lse(ctypes.byref(d), FAKE, 1024, None, None) == bdm.EINVAL and "lse" in err(lib)
+    # topk
+    assert lib.dflash_topk(ctypes.byref(d), FAKE, 1024, FAKE, None, FAKE, FAKE, FAKE, FAKE, 16, None) == \
+        bdm.EWORKSPACE
+    assert lib.dflash_topk(ctypes.byref(dims(target_vocab=2000)), FAKE, 1024, FAKE, None, FAKE, FAKE, FAKE, FAKE,
+                           big, None) == bdm.EINVAL and "d2t" in err(lib)
+    assert lib.dflash_topk(ctypes.byref(d), FAKE, 1024, FAKE, None, None, FAKE, FAKE, FAKE, big, None) == \
+        bdm.EINVAL and "cand_idx" in err(lib)
+    # pair scores: the gate reads the hidden states
+    assert lib.dflash_pair_scores(ctypes.byref(d), FAKE, FAKE, FAKE, None, FAKE, None, FAKE, None) == bdm.EINVAL
+    assert "hidden" in err(lib)
+    assert lib.dflash_pair_scores(ctypes.byref(dims(total_rows=4)), FAKE, FAKE, None, None, FAKE, None, FAKE,
+                                  None) == bdm.EINVAL
+    # walk
+    assert lib.dflash_walk(ctypes.byref(dims(walk=3)), FAKE, FAKE, FAKE, None, FAKE, FAKE, None, None) == \
+        bdm.EINVAL and "walk" in err(lib)
+    assert lib.dflash_walk(ctypes.byref(d), FAKE, FAKE, None, None, FAKE, FAKE, None, None) == bdm.EINVAL
+    assert "pair" in err(lib)
+
+
+def test_check_d2t_host(lib):
+    sub = np.random.default_rng(3).permutation(200)[:48]
+    d2t = np.ascontiguousarray(sub - np.arange(48), dtype=np.int64)
+    inj = ctypes.c_int(-1)
+    assert lib.dflash_check_d2t(d2t.ctypes.data, 48, 200, ctypes.byref(inj)) == bdm.OK and inj.value == 1
+    assert err(lib) == ""
+    dup = d2t.copy()
+    dup[1] = sub[0] - 1
+    assert lib.dflash_check_d2t(dup.ctypes.data, 48, 200, ctypes.byref(inj)) == bdm.OK and inj.value == 0
+    bad = d2t.copy()
+    bad[7] = 500
+    assert lib.dflash_check_d2t(bad.ctypes.data, 48, 200, ctypes.byref(inj)) == bdm.EINVAL
+    assert "d2t[7]" in err(lib)
+    neg = d2t.copy()
+    neg[0] = -1   # maps draft 0 to target -1
+    assert lib.dflash_check_d2t(neg.ctypes.data, 48, 200, ctypes.byref(inj)) == bdm.EINVAL
+    assert lib.dflash_check_d2t(None, 48, 200, ctypes.byref(inj)) == bdm.EINVAL
+    assert lib.dflash_check_d2t(d2t.ctypes.data, 48, 40, ctypes.byref(inj)) == bdm.EINVAL
+
+
+def test_binding_check_d2t_matches_oracle():
+    from block_draft_markov_amd import api
+    from oracle import draft_step as O
+    rng = np.random.default_rng(1)
+    for _ in range(20):
+        Vd, Vt = int(rng.integers(1, 60)), int(rng.integers(60, 120))
+        t = rng.integers(0, Vt, size=Vd)
+        d2t = t - np.arange(Vd)
+        valid, inj = O.check_d2t(d2t, Vd, Vt)
+        assert valid
+        assert api.check_d2t(d2t, Vd, Vt) == inj

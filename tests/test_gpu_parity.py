@@ -1,0 +1,445 @@
+"""GPU parity of the HIP draft step against the CPU oracle, through the C ABI.
+
+Bars (from the draft-step spec):
+  * logits: |z_gpu - z_oracle| <= 1e-3 * max|z_oracle| of the row;
+  * Top-K: the slots are bit-exact when fed the oracle's logits (the same
+    fp32 values on both sides); from the GPU's own logits they are bit-exact
+    unless the oracle's K-th and (K+1)-th logits differ by less than the
+    logit tolerance (then the set rule of gpu_util.check_topk_row applies);
+  * walk: tokens and slots bit-exact when fed the oracle's unary and pairwise
+    values (rounded to fp32, the oracle re-walking those fp32 values in
+    fp64); a case whose oracle runner-up margin is below 1e-6 * max(|S|, 1)
+    is listed as an exemption; path scores within 1e-4 * max(|S|, 1);
+  * integer outputs (ids, target ids, slots) are compared exactly.
+"""
+import numpy as np
+import pytest
+import torch
+
+import draft_inputs as di
+from oracle import draft_step as O
+from tests.gpu_util import (check_topk_row, dev, dev_bf16, logits_tol, offsets_of, pack_pair, require_gpu, say,
+                            upload)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+    from block_draft_markov_amd import api
+    return api
+
+
+def api():
+    from block_draft_markov_amd import api as a
+    return a
+
+
+def f32(x):
+    return np.asarray(x, dtype=np.float32)
+
+
+# ============================================================ part 1: lm_head
+
+LMHEAD_CASES = [
+    # (name, M, H, V)          what it covers
+    ("tiny", 5, 64, 1024),                    # the tiny workload
+    ("ragged", 37, 136, 2051),                # M tail in a 16-row tile, H % 64 != 0, V % 16 and V % 4 != 0
+    ("two_row_chunks", 300, 128, 5000),       # more than 256 rows: two row chunks
+    ("one_row", 1, 64, 17),                   # a single row and a single partial tile
+    ("rows_224", 224, 256, 20000),            # the 224-row tile of the 4B batch
+    ("rows_240", 240, 512, 33333),            # the 240-row tile of the 27B / pruned batches
+]
+
+
+@pytest.mark.parametrize("name,M,H,V", LMHEAD_CASES)
+def test_lm_head_parity(name, M, H, V):
+    say(f"lm_head {name}: M={M} H={H} V={V}")
+    sh = di.custom_shape(name, R=M, L=1, H=H, Vd=V, K=min(64, V), r=4, seed=11 + M)
+    inp = di.make_inputs(sh)
+    z_gpu, lse_gpu = api().lm_head(dev_bf16(inp.hidden), dev_bf16(inp.lm_head))
+    torch.cuda.synchronize()
+    z_gpu = z_gpu.cpu().numpy().astype(np.float64)
+    lse_gpu = lse_gpu.cpu().numpy().astype(np.float64)
+    z = O.logits(inp.hidden, inp.lm_head)
+    lse = O.row_lse(z)
+    worst = 0.0
+    for m in range(M):
+        tol = logits_tol(z[m])
+        err = np.max(np.abs(z_gpu[m] - z[m]))
+        assert err <= tol, f"row {m}: max error {err} > {tol}"
+        worst = max(worst, err / max(np.max(np.abs(z[m])), 1e-30))
+        assert abs(lse_gpu[m] - lse[m]) <= tol
+    say(f"  max relative logit error {worst:.3e}")
+    assert worst < 1e-5   # fp32 accumulation of exact bf16 products: far inside the bar
+
+
+def test_lm_head_full_qwen3_4b_single_request():
+    """All 7 rows of the Qwen3-4B-shaped block at full vocabulary and hidden size."""
+    inp = di.make_inputs(di.SHAPES["qwen3_4b_1"])
+    say("lm_head qwen3_4b_1 full")
+    z_gpu, lse_gpu = api().lm_head(dev_bf16(inp.hidden), dev_bf16(inp.lm_head))
+    z_gpu = z_gpu.cpu().numpy().astype(np.float64)
+    lse_gpu = lse_gpu.cpu().numpy()
+    z = O.logits(inp.hidden, inp.lm_head)
+    lse = O.row_lse(z)
+    for m in range(inp.M):
+        tol = logits_tol(z[m])
+        assert np.max(np.abs(z_gpu[m] - z[m])) <= tol
+        assert abs(lse_gpu[m] - lse[m]) <= tol
+
+
+def test_row_lse_matches_oracle():
+    rng = np.random.default_rng(4)
+    z = (rng.standard_normal((9, 3001)) * 3).astype(np.float32)
+    zt = torch.zeros((9, 3004), dtype=torch.float32, device="cuda")
+    zt[:, :3001] = dev(z)
+    lse = api().row_lse(zt[:, :3001]).cpu().numpy()
+    ref = O.row_lse(z.astype(np.float64))
+    assert np.max(np.abs(lse - ref)) <= 1e-5 * np.max(np.abs(ref))
+
+
+# ============================================================ part 2: Top-K
+
+def _topk_feed(z32: np.ndarray, K: int, d2t=None, Vt=None):
+    """Run dflash_topk on fp32 logits (with the fp64 LSE of those values rounded to fp32)."""
+    M, V = z32.shape
+    ldz = V + (-V) % 4
+    zt = torch.zeros((M, ldz), dtype=torch.float32, device="cuda")
+    zt[:, :V] = dev(z32)
+    lse = O.row_lse(z32.astype(np.float64))
+    idx, tok, un = api().topk(zt[:, :V], dev(f32(lse)), K, d2t=dev(d2t), target_vocab=Vt)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), tok.cpu().numpy(), un.cpu().numpy(), f32(lse)
+
+
+def _check_topk_exact(z32, K, d2t=None, Vt=None):
+    idx, tok, un, lse32 = _topk_feed(z32, K, d2t, Vt)
+    z64 = z32.astype(np.float64)
+    cand = O.candidates(z64, K, d2t)
+    assert np.array_equal(idx, cand.idx), "slots differ from the oracle's full sort"
+    assert np.array_equal(tok, cand.tok), "target ids differ"
+    want = np.take_along_axis(z32, cand.idx, 1).astype(np.float64) - lse32[:, None].astype(np.float64)
+    assert np.max(np.abs(un - want)) <= 1e-6 * max(1.0, np.max(np.abs(want)))
+
+
+TOPK_CASES = [
+    # (name, M, V, K, kind)
+    ("tiny", 5, 1024, 8, "normal"),
+    ("k64", 7, 20000, 64, "normal"),
+    ("k1", 4, 5000, 1, "normal"),
+    ("v_eq_k", 3, 48, 48, "normal"),         # K = V_d: the 48-token draft vocabulary
+    ("v_lt_chunk", 3, 300, 64, "normal"),    # a single short chunk
+    ("ragged_v", 6, 70001, 64, "normal"),    # V % 4 != 0, last chunk partial
+    ("ties_small_ints", 5, 9000, 64, "ints"),     # many exact ties: the radix fallback
+    ("all_equal", 3, 5000, 64, "equal"),          # every logit equal: slots 0..K-1
+    ("signed_zeros", 2, 4096, 64, "zeros"),       # -0.0 and +0.0 tie; the lower id wins
+    ("qwen3_4b_rows", 4, 151936, 64, "normal"),
+    ("dflash2_27b_rows", 3, 248100, 64, "normal"),
+    ("many_rows", 224, 151936, 64, "normal"),     # the row count of the 4B batch: the large-chunk plan
+]
+
+
+def _make_logits(M, V, kind, seed):
+    rng = np.random.default_rng(seed)
+    if kind == "normal":
+        return f32(rng.standard_normal((M, V)))
+    if kind == "ints":
+        return f32(rng.integers(-3, 4, size=(M, V)))
+    if kind == "equal":
+        return np.full((M, V), 0.25, np.float32)
+    if kind == "zeros":
+        z = np.where(rng.random((M, V)) < 0.5, np.float32(0.0), np.float32(-0.0)).astype(np.float32)
+        z[:, ::7] = -1.0
+        return z
+    raise ValueError(kind)
+
+
+@pytest.mark.parametrize("name,M,V,K,kind", TOPK_CASES)
+def test_topk_fed_oracle_logits_bit_exact(name, M, V, K, kind):
+    say(f"topk {name}: M={M} V={V} K={K} {kind}")
+    z32 = _make_logits(M, V, kind, seed=sum(name.encode()))
+    _check_topk_exact(z32, K)
+
+
+def test_topk_pruned_d2t_remap():
+    Vd, Vt = 114688, 248100
+    sub = np.random.default_rng(5).permutation(Vt)[:Vd]
+    d2t = (sub - np.arange(Vd)).astype(np.int64)
+    z32 = _make_logits(5, Vd, "normal", 3)
+    _check_topk_exact(z32, 64, d2t, Vt)
+
+
+def test_topk_48_token_subset():
+    sub = np.random.default_rng(9).permutation(200)[:48]
+    d2t = (sub - np.arange(48)).astype(np.int64)
+    _check_topk_exact(_make_logits(4, 48, "normal", 1), 48, d2t, 200)
+
+
+# ============================================================ part 3: pair scores
+
+PAIR_CASES = [
+    # (name, R, L, K, r, gated, ragged)
+    ("tiny", 1, 5, 8, 16, False, None),
+    ("k64_r256", 3, 7, 64, 256, False, None),
+    ("gated", 2, 15, 64, 256, True, None),
+    ("k5_r100", 3, 4, 5, 100, True, None),     # K % 4 != 0, rank not a multiple of the 64-wide slice
+    ("ragged", 4, 6, 16, 32, False, [3, 0, 6, 1]),
+]
+
+
+@pytest.mark.parametrize("name,R,L,K,r,gated,ragged", PAIR_CASES)
+def test_pair_scores_parity(name, R, L, K, r, gated, ragged):
+    say(f"pair {name}")
+    rng = np.random.default_rng(R * 100 + K)
+    Vt, H = 3000, 64
+    lengths = ragged if ragged is not None else [L] * R
+    off = di.ragged_offsets(lengths)
+    M = int(off[-1])
+    tok = rng.integers(0, Vt, size=(M, K)).astype(np.int64)
+    tables = f32(rng.standard_normal((2, Vt, r)) * 0.25)
+    hidden = di.round_to_bf16_bits(f32(rng.standard_normal((M, H))))
+    w = f32(rng.standard_normal(H) / 8) if gated else None
+    last = rng.integers(0, Vt, size=R).astype(np.int64)
+    pair = api().pair_scores(dev(tok), dev(tables), dev(last), gate_w=dev(w), hidden=dev_bf16(hidden),
+                             row_offsets=dev(off) if ragged is not None else None, block_len=max(lengths))
+    pair = pair.cpu().numpy().astype(np.float64)
+    h64 = O.bf16_to_f64(hidden)
+    for req in range(R):
+        a = int(off[req])
+        S = O.lattice_scores(tok[a:off[req + 1]], tables, h64[a:off[req + 1]], w, int(last[req]))
+        for p, s in enumerate(S):
+            got = pair[a + p, :1, :] if p == 0 else pair[a + p]
+            scale = max(1.0, float(np.max(np.abs(s))))
+            assert np.max(np.abs(got - s)) <= 1e-5 * scale, f"request {req} position {p}"
+            if p == 0:
+                assert np.all(pair[a, 1:, :] == 0.0)
+
+
+# ============================================================ part 4: walk
+
+def _walk_fed(u64, S_all, off, R, K, walk, L):
+    """GPU walk fed the oracle's unary and pairwise values rounded to fp32."""
+    M = u64.shape[0]
+    u32 = f32(u64)
+    pair32 = f32(pack_pair(S_all, off, M, K))
+    tok = np.arange(M * K, dtype=np.int64).reshape(M, K) * 7 + 3    # distinct ids: token = f(row, slot)
+    tokens, scores, slots = api().walk(dev(tok), dev(u32), dev(pair32), R, row_offsets=dev(off.astype(np.int32)),
+                                       block_len=L, walk=walk)
+    return tok, u32, pair32, tokens.cpu().numpy(), scores.cpu().numpy(), slots.cpu().numpy()
+
+
+def _oracle_walk32(u32, pair32, off, R, walk):
+    res = []
+    for req in range(R):
+        a, b = int(off[req]), int(off[req + 1])
+        if b == a:
+            res.append((np.zeros(0, np.int64), 0.0, np.inf))
+            continue
+        u = u32[a:b].astype(np.float64)
+        S = [pair32[a, :1, :].astype(np.float64)] + [pair32[a + p].astype(np.float64) for p in range(1, b - a)]
+        res.append(O.viterbi(u, S) if walk == "viterbi" else O.greedy(u, S))
+    return res
+
+
+def _check_walk(u64, S_all, off, R, K, L, walk):
+    tok, u32, pair32, tokens, scores, slots = _walk_fed(u64, S_all, off, R, K, walk, L)
+    exempt = 0
+    for req, (path, score, margin) in enumerate(_oracle_walk32(u32, pair32, off, R, walk)):
+        a, b = int(off[req]), int(off[req + 1])
+        scale = max(1.0, abs(score))
+        assert abs(scores[req] - score) <= 1e-4 * scale, f"request {req}: score {scores[req]} vs {score}"
+        if b == a:
+            continue
+        if margin < 1e-6 * scale:
+            exempt += 1
+            continue
+        assert list(slots[a:b]) == list(path), f"request {req}: slots differ"
+        assert np.array_equal(tokens[a:b], tok[np.arange(a, b), path])
+    return exempt
+
+
+def _random_lattice(R, lengths, K, seed, scale_pair=1.0, ints=False):
+    rng = np.random.default_rng(seed)
+    M = sum(lengths)
+    if ints:
+        u = rng.integers(-3, 1, size=(M, K)).astype(np.float64)
+    else:
+        u = -np.sort(-rng.standard_normal((M, K)), axis=1) - 5.0
+    S_all, a = [], 0
+    for Lr in lengths:
+        S = []
+        for p in range(Lr):
+            shape = (1, K) if p == 0 else (K, K)
+            S.append(rng.integers(-2, 3, size=shape).astype(np.float64) if ints
+                     else rng.standard_normal(shape) * scale_pair)
+        S_all.append(S)
+        a += Lr
+    return u, S_all, di.ragged_offsets(lengths).astype(np.int64)
+
+
+WALK_CASES = [
+    # (name, lengths, K, kind)
+    ("tiny", [5], 8, "normal"),
+    ("batch_l7_k64", [7] * 32, 64, "normal"),
+    ("batch_l15_k64", [15] * 16, 64, "normal"),
+    ("l1", [1, 1, 1], 64, "normal"),
+    ("k1", [6, 4], 1, "normal"),
+    ("l100", [100, 37], 64, "normal"),          # the maximum block length
+    ("ragged_with_empty", [3, 0, 9, 1, 0], 16, "normal"),
+    ("exact_ties", [6] * 20, 4, "ints"),         # small integers: exact ties in fp32 and fp64
+    ("exact_ties_k64", [7] * 8, 64, "ints"),
+]
+
+
+@pytest.mark.parametrize("walk", ["viterbi", "greedy"])
+@pytest.mark.parametrize("name,lengths,K,kind", WALK_CASES)
+def test_walk_fed_oracle_values_bit_exact(name, lengths, K, kind, walk):
+    say(f"walk {name} {walk}")
+    R = len(lengths)
+    u, S_all, off = _random_lattice(R, lengths, K, seed=len(name) * 31 + K, ints=(kind == "ints"))
+    exempt = _check_walk(u, S_all, off, R, K, max(max(lengths), 1), walk)
+    say(f"  exemptions: {exempt}")
+    assert exempt == 0 or kind == "ints"   # exact ties are compared bit for bit; margins 0 only there
+
+
+# ============================================================ the whole step
+
+def _staged(api_, d, inp, K, L, walk):
+    z, lse = api_.lm_head(d["hidden"], d["lm_head"])
+    idx, tok, un = api_.topk(z, lse, K, d2t=d["d2t"], target_vocab=inp.tables.shape[1])
+    pair = api_.pair_scores(tok, d["tables"], d["last_tok"], gate_w=d["gate_w"], hidden=d["hidden"],
+                            row_offsets=d["row_offsets"], block_len=L)
+    tokens, scores, slots = api_.walk(tok, un, pair, len(inp.last_tok), row_offsets=d["row_offsets"],
+                                      block_len=L, walk=walk)
+    return z, lse, idx, tok, un, tokens, scores, slots
+
+
+def _end_to_end(inp, sample_requests, walk="viterbi"):
+    api_ = api()
+    s = inp.shape
+    R, M, K = len(inp.last_tok), inp.M, s.K
+    off = offsets_of(R, M, inp.row_offsets)
+    L = int(np.max(np.diff(off))) if R else 1
+    d = upload(inp)
+    tokens, scores = api_.draft_block(d["hidden"], d["lm_head"], d["tables"], d["last_tok"], top_k=K, d2t=d["d2t"],
+                                      gate_w=d["gate_w"], row_offsets=d["row_offsets"], block_len=L, walk=walk)
+    tokens2, scores2 = api_.draft_block(d["hidden"], d["lm_head"], d["tables"], d["last_tok"], top_k=K,
+                                        d2t=d["d2t"], gate_w=d["gate_w"], row_offsets=d["row_offsets"],
+                                        block_len=L, walk=walk)
+    z, lse, idx, tok, un, st_tokens, st_scores, st_slots = _staged(api_, d, inp, K, L, walk)
+    torch.cuda.synchronize()
+    tokens, scores = tokens.cpu().numpy(), scores.cpu().numpy()
+    # deterministic, and the fused call equals the staged calls bit for bit
+    assert np.array_equal(tokens, tokens2.cpu().numpy()) and np.array_equal(scores, scores2.cpu().numpy())
+    assert np.array_equal(tokens, st_tokens.cpu().numpy())
+    assert np.array_equal(scores, st_scores.cpu().numpy())
+    idx = idx.cpu().numpy()
+    gtok = tok.cpu().numpy()
+    un = un.cpu().numpy()
+    slots = st_slots.cpu().numpy()
+    counts = dict(rows_exact=0, rows_exempt=0, req_exact=0, req_exempt=0)
+    for req in sample_requests:
+        a, b = int(off[req]), int(off[req + 1])
+        if b == a:
+            assert scores[req] == 0.0
+            continue
+        rows = np.arange(a, b)
+        zo = O.logits(inp.hidden[rows], inp.lm_head)
+        zg = z[a:b].cpu().numpy().astype(np.float64)
+        exempt_rows = 0
+        for i in range(b - a):
+            assert np.max(np.abs(zg[i] - zo[i])) <= logits_tol(zo[i])
+            kind = check_topk_row(idx[a + i], zo[i], K)
+            exempt_rows += kind == "exempt"
+        counts["rows_exact"] += (b - a) - exempt_rows
+        counts["rows_exempt"] += exempt_rows
+        sub = O.draft_from_logits(zo, K, inp.d2t, inp.tables, inp.hidden[rows], inp.gate_w, inp.last_tok[req:req + 1],
+                                  walk=O.WALK_VITERBI if walk == "viterbi" else O.WALK_GREEDY)
+        score, margin = sub.scores[0], sub.margins[0]
+        scale = max(1.0, abs(score))
+        if exempt_rows == 0 and margin >= 1e-5 * scale:
+            assert np.array_equal(tokens[a:b], sub.tokens), f"request {req}: tokens differ"
+            assert abs(scores[req] - score) <= 1e-4 * scale
+            counts["req_exact"] += 1
+        else:
+            # the GPU's own candidate set, re-walked by the oracle in fp64: same best score within 1e-4
+            cand = O.Candidates(idx[a:b].astype(np.int64), gtok[a:b], np.take_along_axis(zo, idx[a:b].astype(np.int64), 1)
+                                - O.row_lse(zo)[:, None], None, O.row_lse(zo), None)
+            alt = O.walk_from_candidates(cand, inp.tables, inp.hidden[rows], inp.gate_w, inp.last_tok[req:req + 1],
+                                         walk=O.WALK_VITERBI if walk == "viterbi" else O.WALK_GREEDY)
+            gpu_path_score = O.path_score(cand.unary, alt.S[0], slots[a:b])
+            assert abs(gpu_path_score - alt.scores[0]) <= 1e-4 * max(1.0, abs(alt.scores[0]))
+            assert abs(scores[req] - alt.scores[0]) <= 1e-4 * max(1.0, abs(alt.scores[0]))
+            counts["req_exempt"] += 1
+    say(f"  {counts}")
+    return counts
+
+
+def test_end_to_end_tiny():
+    c = _end_to_end(di.make_inputs(di.SHAPES["tiny"]), [0])
+    assert c["req_exact"] == 1
+
+
+@pytest.mark.parametrize("walk", ["viterbi", "greedy"])
+def test_end_to_end_tiny_stress_seeds(walk):
+    exact = 0
+    for seed in range(2000, 2040):
+        sh = di.custom_shape("tiny_stress", R=1, L=5, H=64, Vd=1024, K=8, r=16, table_std=0.5, seed=seed,
+                             weight_seed=seed)
+        exact += _end_to_end(di.make_inputs(sh), [0], walk)["req_exact"]
+    assert exact >= 36
+
+
+def test_end_to_end_gated_tiny_and_ragged():
+    sh = di.custom_shape("gated_tiny", R=4, L=6, H=64, Vd=2000, K=16, r=16, gated=True, table_std=0.5, seed=7)
+    inp = di.make_inputs(sh)
+    _end_to_end(inp, range(4))
+    inp.row_offsets = di.ragged_offsets([6, 0, 2, 5])
+    inp.hidden = inp.hidden[:13].copy()
+    _end_to_end(inp, range(4))
+
+
+def test_end_to_end_pruned_small_48():
+    sh = di.custom_shape("pruned48", R=2, L=4, H=64, Vd=48, Vt=200, K=48, r=8, pruned=True, table_std=0.5, seed=9)
+    _end_to_end(di.make_inputs(sh), [0, 1])
+
+
+def test_end_to_end_qwen3_4b_single_request():
+    _end_to_end(di.make_inputs(di.SHAPES["qwen3_4b_1"]), [0])
+
+
+def test_end_to_end_qwen3_4b_batch_sampled():
+    c = _end_to_end(di.make_inputs(di.SHAPES["qwen3_4b_32"]), [0, 13, 31])
+    assert c["req_exact"] + c["req_exempt"] == 3
+
+
+def test_end_to_end_dflash2_27b_sampled():
+    _end_to_end(di.make_inputs(di.SHAPES["dflash2_27b"]), [0, 15])
+
+
+def test_end_to_end_pruned_ocr_sampled():
+    _end_to_end(di.make_inputs(di.SHAPES["pruned_ocr"]), [2, 9])
+
+
+def test_empty_batch_is_a_no_op():
+    sh = di.custom_shape("empty", R=0, L=3, H=64, Vd=1024, K=8, r=4, seed=1)
+    inp = di.make_inputs(sh)
+    d = upload(inp)
+    tokens, scores = api().draft_block(d["hidden"], d["lm_head"], d["tables"], d["last_tok"], top_k=8, block_len=3)
+    torch.cuda.synchronize()
+    assert tokens.numel() == 0 and scores.numel() == 0
+
+
+def test_request_isolation_on_gpu():
+    sh = di.custom_shape("iso", R=3, L=4, H=64, Vd=3000, K=16, r=16, table_std=0.5, seed=21)
+    inp = di.make_inputs(sh)
+    d = upload(inp)
+    t1, s1 = api().draft_block(d["hidden"], d["lm_head"], d["tables"], d["last_tok"], top_k=16)
+    h2 = inp.hidden.copy()
+    h2[4:8] = di.round_to_bf16_bits(f32(np.random.default_rng(2).standard_normal((4, 64))))
+    t2, s2 = api().draft_block(dev_bf16(h2), d["lm_head"], d["tables"], d["last_tok"], top_k=16)
+    t1, t2, s1, s2 = (x.cpu().numpy() for x in (t1, t2, s1, s2))
+    keep = np.r_[0:4, 8:12]
+    assert np.array_equal(t1[keep], t2[keep]) and s1[0] == s2[0] and s1[2] == s2[2]
