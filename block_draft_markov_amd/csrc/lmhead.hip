@@ -221,6 +221,7 @@ hipError_t launch_mt(const LmHeadArgs& a, dim3 grid, hipStream_t s) {
 }
 
 int row_tiles_per_chunk(int M) {
+    if (M <= 0) return 1;
     const int gy = (M + 255) / 256;
     const int rows = (M + gy - 1) / gy;
     return (rows + 15) / 16;

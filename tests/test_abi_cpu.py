@@ -117,6 +117,21 @@ def test_draft_block_pointer_and_mode_rules(lib):
     assert call(hidden=FAKE + 2) == bdm.EINVAL and "aligned" in err(lib)
 
 
+@pytest.mark.parametrize("R,L,M", [(0, 3, 0), (2, 5, 0), (1, 1, 1), (400, 1, 400)])
+def test_workspace_sizing_edge_rows(lib, R, L, M):
+    # empty batches, a single row and more rows than one 256-row chunk size without faults
+    n = lib.dflash_workspace_bytes(ctypes.byref(dims(num_requests=R, block_len=L, total_rows=M)))
+    assert n >= 256 and n % 256 == 0
+
+
+def test_empty_batch_returns_before_any_launch(lib):
+    # M = 0 rows: nothing to launch, every array may be NULL; a NULL stream is never used
+    d = dims(num_requests=0, block_len=3, total_rows=0)
+    need = lib.dflash_workspace_bytes(ctypes.byref(d))
+    assert lib.dflash_draft_block(ctypes.byref(d), None, FAKE, None, FAKE, None, None, None, None, None, FAKE,
+                                  need, None) == bdm.OK
+
+
 def test_stage_entry_points_validate(lib):
     d = dims()
     big = 1 << 40
