@@ -98,7 +98,7 @@ Layout layout(const dflash_dims* d) {
     Layout l{};
     const int64_t M = d->total_rows, K = d->top_k;
     l.ldz = round_up(d->draft_vocab, 4);
-    l.nparts = dflash::lmhead_grid_x(d->total_rows, d->draft_vocab);
+    l.nparts = dflash::lmhead_partials(d->total_rows, d->draft_vocab);
     const dflash::TopkPlan p = dflash::topk_plan(d->total_rows, d->draft_vocab, d->top_k);
     size_t off = 0;
     auto take = [&](size_t bytes) {

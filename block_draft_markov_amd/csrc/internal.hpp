@@ -10,8 +10,7 @@ namespace dflash {
 // ---------------------------------------------------------------- part 1: lm_head GEMM
 // Vocabulary rows are handled in tiles of 16; a workgroup owns a contiguous
 // range of tiles and keeps one (max, sum exp) partial per row.
-int lmhead_grid_x(int M, int V);          // workgroups along the vocabulary
-int lmhead_grid_y(int M);                 // workgroups along the rows
+int lmhead_partials(int M, int V);       // (max, sum exp) partials per row
 hipError_t launch_lmhead(const uint16_t* hidden, const uint16_t* W, float* logits, int64_t ldz,
                          float2* lse_part, int M, int H, int V, hipStream_t s);
 // lse[m] from the partials of row m.

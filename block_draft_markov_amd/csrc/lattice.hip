@@ -97,14 +97,50 @@ __global__ void __launch_bounds__(kPairThreads) pair_scores_kernel(
 #pragma unroll
         for (int y = 0; y < 4; ++y) acc[x][y] = 0.f;
 
-    for (int i0 = 0; i0 < r; i0 += kSlice) {
-        for (int idx = tid; idx < 64 * kSlice; idx += kPairThreads) {
-            const int row = idx / kSlice, col = idx % kSlice;
-            const bool in = i0 + col < r;
-            As[col][row] = (row < Jn && in) ? TA[prev_row[row] + i0 + col] : 0.f;
-            Bs[col][row] = (row < K && in) ? TB[cand_row[row] + i0 + col] : 0.f;
+    // Gather of one 64-wide rank slice: row `row` of A (previous tokens) and of B
+    // (candidates), elements i0 .. i0+63.  With r % 4 == 0 the rows are 16-byte
+    // aligned and every thread loads 4 float4 of A and 4 of B; the next slice is
+    // in flight while the current one is multiplied.
+    const bool vec = (r & 3) == 0 && (reinterpret_cast<uintptr_t>(tables) & 15) == 0;
+    f32x4 ra[4], rb[4];
+    auto gather = [&](int i0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int f4 = tid + i * kPairThreads;          // 0 .. 1023
+            const int row = f4 >> 4, c = (f4 & 15) * 4;     // 16 float4 per 64-wide row slice
+            f32x4 va = {0.f, 0.f, 0.f, 0.f}, vb = {0.f, 0.f, 0.f, 0.f};
+            if (vec) {
+                if (row < Jn && i0 + c < r) va = *reinterpret_cast<const f32x4*>(TA + prev_row[row] + i0 + c);
+                if (row < K && i0 + c < r) vb = *reinterpret_cast<const f32x4*>(TB + cand_row[row] + i0 + c);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if (row < Jn && i0 + c + e < r) va[e] = TA[prev_row[row] + i0 + c + e];
+                    if (row < K && i0 + c + e < r) vb[e] = TB[cand_row[row] + i0 + c + e];
+                }
+            }
+            ra[i] = va;
+            rb[i] = vb;
         }
+    };
+    auto stash = [&]() {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int f4 = tid + i * kPairThreads;
+            const int row = f4 >> 4, c = (f4 & 15) * 4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                As[c + e][row] = ra[i][e];
+                Bs[c + e][row] = rb[i][e];
+            }
+        }
+    };
+
+    gather(0);
+    for (int i0 = 0; i0 < r; i0 += kSlice) {
+        stash();
         __syncthreads();
+        if (i0 + kSlice < r) gather(i0 + kSlice);
 #pragma unroll 8
         for (int ii = 0; ii < kSlice; ++ii) {
             const f32x4 av = *reinterpret_cast<const f32x4*>(&As[ii][4 * tj]);
@@ -148,12 +184,18 @@ __global__ void __launch_bounds__(64) walk_kernel(const int64_t* __restrict__ ca
     float score;
     if (walk == DFLASH_WALK_VITERBI) {
         float d = act ? unary[(int64_t)a * K + lane] + pair[(int64_t)a * K * K + lane] : -INFINITY;
-        for (int p = 1; p < n; ++p) {
+        // lane k needs column k of S_p (64 strided floats) and u_p[k]; the column of
+        // position p+1 is loaded while position p is folded in
+        float colA[64], colB[64];
+        float uA = 0.f, uB = 0.f;
+        auto load_col = [&](int p, float (&col)[64], float& u) {
             const int64_t m = a + p;
             const float* S = pair + m * K * K;
-            float col[64];
 #pragma unroll
             for (int j = 0; j < 64; ++j) col[j] = (j < K && act) ? S[j * K + lane] : 0.f;
+            u = act ? unary[m * K + lane] : 0.f;
+        };
+        auto fold = [&](int p, const float (&col)[64], float u) {
             float best = -INFINITY;
             int arg = 0;
 #pragma unroll
@@ -164,8 +206,17 @@ __global__ void __launch_bounds__(64) walk_kernel(const int64_t* __restrict__ ca
                     if (v > best) { best = v; arg = j; }
                 }
             }
-            d = act ? unary[m * K + lane] + best : -INFINITY;
+            d = act ? u + best : -INFINITY;
             back[p][lane] = (uint8_t)arg;
+        };
+        if (n > 1) load_col(1, colA, uA);
+        for (int p = 1; p < n; p += 2) {
+            if (p + 1 < n) load_col(p + 1, colB, uB);
+            fold(p, colA, uA);
+            if (p + 1 < n) {
+                if (p + 2 < n) load_col(p + 2, colA, uA);
+                fold(p + 1, colB, uB);
+            }
         }
         score = wave_max(d);
         // NaN scores match no lane: fall back to slot 0 rather than index past the slots

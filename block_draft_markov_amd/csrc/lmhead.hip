@@ -31,6 +31,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 namespace dflash {
 
 namespace {
@@ -38,7 +40,8 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kBK = 64;                       // h elements per stage
 constexpr int kRowBytes = kBK * 2 + 16;       // padded LDS row: conflict-free 16-byte reads
-constexpr int kNT = 4;                        // vocab tiles per wave per pass
+constexpr int kNT = 4;      // vocab tiles per wave per pass of the small-row kernel
+constexpr int kDepth = 4;   // its W register ring
 
 struct LmHeadArgs {
     const uint16_t* hidden;
@@ -47,9 +50,25 @@ struct LmHeadArgs {
     float2* part;
     int64_t ldz;
     int M, H, V;
-    int tiles;   // ceil(V / 16)
+    int tiles;   // vocab tiles: ceil(V / 16) for the small-row kernel, ceil(V / 32) for the batched one
     int G;       // workgroups along the vocabulary
 };
+
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for_impl(F&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for_impl<I + 1, N>(f);
+    }
+}
+// f(integral_constant<0>) ... f(integral_constant<N-1>), unrolled at compile time
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) { static_for_impl<0, N>(f); }
+
+constexpr int gcd_c(int x, int y) { return y == 0 ? x : gcd_c(y, x % y); }
+constexpr int lcm3(int x, int y, int z) {
+    return (x / gcd_c(x, y) * y) / gcd_c(x / gcd_c(x, y) * y, z) * z;
+}
 
 __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
     if (s2 == 0.f) return;
@@ -59,12 +78,14 @@ __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2
     m = mn;
 }
 
-template <int MT, int NT>
+template <int MT, int NT, int DEPTH>
 __global__ void __launch_bounds__(kThreads) lmhead_gemm_lse_kernel(LmHeadArgs a) {
     constexpr int ROWS = MT * 16;
     constexpr int CHUNKS = ROWS * (kBK / 8);                  // 16-byte pieces of a hidden stage
     constexpr int PER_THREAD = (CHUNKS + kThreads - 1) / kThreads;
-    __shared__ __attribute__((aligned(16))) uint8_t hs[2][ROWS][kRowBytes];
+    // one spare row takes the writes of the surplus threads of the last hidden
+    // chunk round, so that stores need no branch
+    __shared__ __attribute__((aligned(16))) uint8_t hs[2][ROWS + 1][kRowBytes];
     __shared__ float2 wpart[4][ROWS];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -78,24 +99,26 @@ __global__ void __launch_bounds__(kThreads) lmhead_gemm_lse_kernel(LmHeadArgs a)
 
     float run_m = 0.f, run_s = 0.f;   // running LSE partial of row m0 + tid (s == 0: empty)
 
-    // hidden stage ks -> registers
-    auto load_h = [&](int ks, bf16x8 (&reg)[PER_THREAD]) {
+    // hidden stage ks -> registers.  Loads are never skipped or masked at load
+    // time: an out-of-range piece loads a clamped, valid address and is zeroed
+    // when it is written to LDS.  (A branch or a select right after a load makes
+    // the compiler wait for that load at once, which would serialise the pipeline.)
+    auto load_h = [&](int ks, bf16x8 (&reg)[PER_THREAD]) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < PER_THREAD; ++i) {
             const int c = tid + i * kThreads;
             const int row = c >> 3, col = ks * kBK + (c & 7) * 8;
-            bf16x8 v = {};
-            if (c < CHUNKS && m0 + row < a.M && col < H)
-                v = *reinterpret_cast<const bf16x8*>(a.hidden + (int64_t)(m0 + row) * H + col);
-            reg[i] = v;
+            const int grow = min(m0 + row, a.M - 1), gcol = min(col, H - 8);
+            reg[i] = *reinterpret_cast<const bf16x8*>(a.hidden + (int64_t)grow * H + gcol);
         }
     };
-    auto store_h = [&](int buf, const bf16x8 (&reg)[PER_THREAD]) {
+    auto store_h = [&](int buf, int ks, const bf16x8 (&reg)[PER_THREAD]) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < PER_THREAD; ++i) {
             const int c = tid + i * kThreads;
-            if (c < CHUNKS)
-                *reinterpret_cast<bf16x8*>(&hs[buf][c >> 3][(c & 7) * 16]) = reg[i];
+            const int row = c >> 3, col = ks * kBK + (c & 7) * 8;
+            const bool ok = c < CHUNKS && m0 + row < a.M && col < H;
+            *reinterpret_cast<bf16x8*>(&hs[buf][min(row, ROWS)][(c & 7) * 16]) = ok ? reg[i] : bf16x8{};
         }
     };
 
@@ -111,15 +134,14 @@ __global__ void __launch_bounds__(kThreads) lmhead_gemm_lse_kernel(LmHeadArgs a)
             v = min(v, a.V - 1);   // rows past the vocabulary load a valid row; their results are dropped
             wrow[j] = reinterpret_cast<const bf16x8*>(a.W + (int64_t)v * H);
         }
-        auto load_w = [&](int ks, bf16x8 (&w)[NT][2]) {
+        auto load_w = [&](int ks, bf16x8 (&w)[NT][2]) __attribute__((always_inline)) {
 #pragma unroll
             for (int j = 0; j < NT; ++j) {
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
                     const int col = ks * kBK + lg * 16 + s * 8;
-                    bf16x8 v = {};
-                    if (tvalid[j] && col < H) v = __builtin_nontemporal_load(wrow[j] + (col >> 3));
-                    w[j][s] = v;
+                    // columns past H meet zeroed hidden values; rows of invalid tiles are dropped
+                    w[j][s] = __builtin_nontemporal_load(wrow[j] + (min(col, H - 8) >> 3));
                 }
             }
         };
@@ -130,38 +152,59 @@ __global__ void __launch_bounds__(kThreads) lmhead_gemm_lse_kernel(LmHeadArgs a)
 #pragma unroll
             for (int j = 0; j < NT; ++j) acc[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-        bf16x8 hreg[PER_THREAD];
-        bf16x8 wcur[NT][2], wnext[NT][2];
-        load_h(0, hreg);
-        load_w(0, wcur);
-        store_h(0, hreg);
+        // Software pipeline over 64-wide h steps.  W(s) is loaded at step s-(DEPTH-1) into
+        // wbuf[s % DEPTH]; hidden(s) is loaded at step s-2 into hreg[s % 2] and written to
+        // LDS buffer s % 2 at the end of step s-1.  Every W load is issued after the hidden
+        // load that the next LDS write waits for, so that wait never forces a young W load.
+        bf16x8 hreg[2][PER_THREAD];
+        bf16x8 wbuf[DEPTH][NT][2];
+        load_h(0, hreg[0]);
+        load_h(1, hreg[1]);
+#pragma unroll
+        for (int d = 0; d < DEPTH - 1; ++d) load_w(d, wbuf[d]);
+        store_h(0, 0, hreg[0]);
         __syncthreads();
 
-        for (int ks = 0; ks < nks; ++ks) {
-            const int buf = ks & 1;
-            const bool more = ks + 1 < nks;
-            if (more) {
-                load_h(ks + 1, hreg);
-                load_w(ks + 1, wnext);
-            }
+        // one 64-wide step: prefetch hidden(ks+2) and W(ks+DEPTH-1), multiply step ks,
+        // write hidden(ks+1) to LDS.  In the main loop nothing is conditional
+        // (prefetches past the end read clamped addresses and are never used), so
+        // the compiler can count outstanding loads exactly.
+        auto step = [&](auto U, int ks) __attribute__((always_inline)) {
+            constexpr int u = decltype(U)::value;
+            load_h(ks + 2, hreg[u & 1]);
+            load_w(ks + DEPTH - 1, wbuf[(u + DEPTH - 1) % DEPTH]);
+            // the B fragments of row tile mt+1 are read from LDS while tile mt multiplies
+            const uint8_t* base = &hs[u & 1][lr][lg * 32];
+            bf16x8 hb[2][2];
+            hb[0][0] = *reinterpret_cast<const bf16x8*>(base);
+            hb[0][1] = *reinterpret_cast<const bf16x8*>(base + 16);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                const uint8_t* rowp = &hs[buf][mt * 16 + lr][lg * 32];
-                const bf16x8 h0 = *reinterpret_cast<const bf16x8*>(rowp);
-                const bf16x8 h1 = *reinterpret_cast<const bf16x8*>(rowp + 16);
-#pragma unroll
-                for (int j = 0; j < NT; ++j) {
-                    acc[mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wcur[j][0], h0, acc[mt][j], 0, 0, 0);
-                    acc[mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wcur[j][1], h1, acc[mt][j], 0, 0, 0);
+                if (mt + 1 < MT) {
+                    const uint8_t* rowp = base + (mt + 1) * 16 * kRowBytes;
+                    hb[(mt + 1) & 1][0] = *reinterpret_cast<const bf16x8*>(rowp);
+                    hb[(mt + 1) & 1][1] = *reinterpret_cast<const bf16x8*>(rowp + 16);
                 }
-            }
-            if (more) store_h(buf ^ 1, hreg);
-            __syncthreads();
-            if (more) {
 #pragma unroll
-                for (int j = 0; j < NT; ++j) { wcur[j][0] = wnext[j][0]; wcur[j][1] = wnext[j][1]; }
+                for (int j = 0; j < NT; ++j)
+                    acc[mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wbuf[u % DEPTH][j][0], hb[mt & 1][0], acc[mt][j], 0, 0, 0);
+#pragma unroll
+                for (int j = 0; j < NT; ++j)
+                    acc[mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wbuf[u % DEPTH][j][1], hb[mt & 1][1], acc[mt][j], 0, 0, 0);
             }
+            store_h((u + 1) & 1, ks + 1, hreg[(u + 1) & 1]);
+            __syncthreads();
+        };
+        // UN steps per iteration keep every ring slot a compile-time register choice
+        constexpr int UN = (DEPTH % 2 == 0) ? DEPTH : 2 * DEPTH;
+        const int nmain = nks - nks % UN;
+        for (int ks0 = 0; ks0 < nmain; ks0 += UN) {
+            static_for<UN>([&](auto U) __attribute__((always_inline)) { step(U, ks0 + decltype(U)::value); });
         }
+        // the remaining steps use the same slots, since nmain is a multiple of UN
+        static_for<UN - 1>([&](auto U) __attribute__((always_inline)) {
+            if (nmain + decltype(U)::value < nks) step(U, nmain + decltype(U)::value);
+        });
 
         // ---- epilogue of the pass: store logits, fold the rows' (max, sum exp) partials
 #pragma unroll
@@ -192,7 +235,7 @@ __global__ void __launch_bounds__(kThreads) lmhead_gemm_lse_kernel(LmHeadArgs a)
                 const int v0 = (pt + wave + 4 * j) * 16 + lg * 4;
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
-                    if (tvalid[j] && v0 + q < a.V) sm += expf(acc[mt][j][q] - mx);
+                    if (tvalid[j] && v0 + q < a.V) sm += __expf(acc[mt][j][q] - mx);
             }
             // the four lanes lr, lr+16, lr+32, lr+48 hold the same row
 #pragma unroll
@@ -214,17 +257,245 @@ __global__ void __launch_bounds__(kThreads) lmhead_gemm_lse_kernel(LmHeadArgs a)
         a.part[(int64_t)(m0 + tid) * a.G + b] = make_float2(run_m, run_s);
 }
 
+// ---------------------------------------------------------------- batched row tiles
+// More than 64 rows: a warp-specialised kernel.  Of the 8 waves of a
+// workgroup, waves 4..7 are producers: they only move data, W rows of the
+// pass and the hidden rows of the batch, from HBM and L2 into a 3-slot LDS
+// ring, through a register ring that keeps loads STEP_AHEAD 64-wide steps in
+// flight.  Waves 0..3 are consumers: they only read MFMA operands from LDS
+// and issue v_mfma_f32_32x32x16_bf16 (on gfx950 it sustains about 2.2
+// PFLOP/s with two accumulator chains; the 16x16x32 form reaches barely
+// half).  A producer's wait for its loads therefore never stalls an MFMA,
+// and memory and matrix work overlap instead of adding up.
+// Consumer w owns vocab tile w (32 rows) of every pass and all MT 32-row
+// tiles of the batch.  Operands: lane l covers row l % 32 and, in sub-step s
+// of a 64-wide step, reduction indices 64 ks + 32 (l / 32) + 8 s .. +7, the
+// same in A (W) and B (hidden).  Result register r of lane l is vocab entry
+// 8 (r / 4) + 4 (l / 32) + r % 4 of the tile for batch row l % 32, so a lane
+// stores four runs of four consecutive logits.
+// LDS rows are 128 bytes with the 16-byte chunk c of row r kept at chunk
+// c ^ swz(r), which makes the fragment reads conflict-free for 32- and
+// 64-bank LDS without padding.
+constexpr int kPcThreads = 512;
+constexpr int kConsumers = 4;
+constexpr int kSlots = 3;
+constexpr int kStepAhead = 3;
+
+__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
+
+template <int MT>
+__global__ void __launch_bounds__(kPcThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+lmhead_pc_kernel(LmHeadArgs a) {
+    constexpr int BN = kConsumers * 32;              // vocab rows per pass
+    constexpr int HR = MT * 32;                      // batch rows staged
+    constexpr int WP = BN * 8 / 256;                 // W pieces per producer thread per step
+    constexpr int HP = (HR * 8 + 255) / 256;         // hidden pieces per producer thread per step
+    __shared__ __attribute__((aligned(16))) uint8_t wsm[kSlots][BN][128];
+    __shared__ __attribute__((aligned(16))) uint8_t hsm[kSlots][HR][128];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lr = lane & 31, lh = lane >> 5;
+    const int b = blockIdx.x;
+    const int m0 = blockIdx.y * HR;                  // first batch row of this row chunk
+    const int t_begin = (int)((int64_t)b * a.tiles / a.G);
+    const int t_end = (int)((int64_t)(b + 1) * a.tiles / a.G);
+    const int H = a.H;
+    const int nks = (H + kBK - 1) / kBK;
+    const int hchunks = H / 8;
+
+    // Both roles walk the same passes and steps, with one barrier per step plus one per pass,
+    // so their __syncthreads calls pair up.
+    if (wave >= kConsumers) {
+        // ================= producers: HBM / L2 -> registers -> LDS ring
+        const int ptid = tid - kConsumers * 64;      // 0..255
+        const int pc = ptid & 7;                     // 16-byte chunk of the pieces of this thread
+        const uint16_t* hsrc[HP];
+#pragma unroll
+        for (int q = 0; q < HP; ++q) {
+            const int row = (ptid + 256 * q) >> 3;
+            hsrc[q] = a.hidden + (int64_t)min(m0 + row, a.M - 1) * H;
+        }
+        for (int pt = t_begin; pt < t_end; pt += kConsumers) {
+            const bf16x8* wsrc[WP];
+#pragma unroll
+            for (int q = 0; q < WP; ++q) {
+                const int v = min(pt * 32 + ((ptid + 256 * q) >> 3), a.V - 1);
+                wsrc[q] = reinterpret_cast<const bf16x8*>(a.W + (int64_t)v * H);
+            }
+            auto load_step = [&](int ks, bf16x8 (&rw)[WP], bf16x8 (&rh)[HP]) __attribute__((always_inline)) {
+                const int chunk = min(ks * 8 + pc, hchunks - 1);
+#pragma unroll
+                for (int q = 0; q < WP; ++q) rw[q] = __builtin_nontemporal_load(wsrc[q] + chunk);
+#pragma unroll
+                for (int q = 0; q < HP; ++q) rh[q] = *reinterpret_cast<const bf16x8*>(hsrc[q] + chunk * 8);
+            };
+            auto store_step = [&](int slot, int ks, const bf16x8 (&rw)[WP], const bf16x8 (&rh)[HP])
+                __attribute__((always_inline)) {
+                const bool colok = ks * kBK + pc * 8 < H;    // columns past H are zero
+#pragma unroll
+                for (int q = 0; q < WP; ++q) {
+                    const int row = (ptid + 256 * q) >> 3;
+                    *reinterpret_cast<bf16x8*>(&wsm[slot][row][(pc ^ swz(row)) * 16]) = colok ? rw[q] : bf16x8{};
+                }
+#pragma unroll
+                for (int q = 0; q < HP; ++q) {
+                    const int row = (ptid + 256 * q) >> 3;
+                    const bool ok = colok && m0 + row < a.M;
+                    *reinterpret_cast<bf16x8*>(&hsm[slot][row][(pc ^ swz(row)) * 16]) = ok ? rh[q] : bf16x8{};
+                }
+            };
+            bf16x8 rw[kStepAhead][WP], rh[kStepAhead][HP];
+            // prologue: steps 0 .. kStepAhead-1 in flight, step 0 written to slot 0
+            static_for<kStepAhead>([&](auto D) __attribute__((always_inline)) {
+                load_step(decltype(D)::value, rw[decltype(D)::value], rh[decltype(D)::value]);
+            });
+            store_step(0, 0, rw[0], rh[0]);
+            __syncthreads();
+            // step ks: refill ring entry ks % kStepAhead with step ks + kStepAhead, then write
+            // step ks + 1 (loaded kStepAhead - 1 steps ago) into slot (ks + 1) % kSlots
+            auto pstep = [&](auto U, int ks) __attribute__((always_inline)) {
+                constexpr int u = decltype(U)::value;
+                load_step(ks + kStepAhead, rw[u % kStepAhead], rh[u % kStepAhead]);
+                store_step((u + 1) % kSlots, ks + 1, rw[(u + 1) % kStepAhead], rh[(u + 1) % kStepAhead]);
+                __syncthreads();
+            };
+            constexpr int UN = lcm3(kStepAhead, kSlots, 1);
+            const int nmain = nks - nks % UN;
+            for (int ks0 = 0; ks0 < nmain; ks0 += UN)
+                static_for<UN>([&](auto U) __attribute__((always_inline)) { pstep(U, ks0 + decltype(U)::value); });
+            static_for<UN - 1>([&](auto U) __attribute__((always_inline)) {
+                if (nmain + decltype(U)::value < nks) pstep(U, nmain + decltype(U)::value);
+            });
+        }
+    } else {
+        // ================= consumers: LDS -> MFMA, then the pass epilogue
+        float run_m[MT], run_s[MT];
+#pragma unroll
+        for (int i = 0; i < MT; ++i) { run_m[i] = 0.f; run_s[i] = 0.f; }
+        for (int pt = t_begin; pt < t_end; pt += kConsumers) {
+            const int tile = pt + wave;                  // this wave's vocab tile
+            const bool cvalid = tile < t_end;
+            f32x16 acc[MT];
+#pragma unroll
+            for (int i = 0; i < MT; ++i) acc[i] = f32x16{};
+            __syncthreads();   // pairs with the producers' prologue barrier
+            auto cstep = [&](auto U, int ks) __attribute__((always_inline)) {
+                constexpr int slot = decltype(U)::value % kSlots;
+                if (cvalid) {
+                    bf16x8 af[4];
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        const int r = wave * 32 + lr;
+                        af[s] = *reinterpret_cast<const bf16x8*>(&wsm[slot][r][((4 * lh + s) ^ swz(r)) * 16]);
+                    }
+#pragma unroll
+                    for (int i = 0; i < MT; ++i) {
+                        const int r = i * 32 + lr;
+                        bf16x8 hb[4];
+#pragma unroll
+                        for (int s = 0; s < 4; ++s)
+                            hb[s] = *reinterpret_cast<const bf16x8*>(&hsm[slot][r][((4 * lh + s) ^ swz(r)) * 16]);
+#pragma unroll
+                        for (int s = 0; s < 4; ++s)
+                            acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s], hb[s], acc[i], 0, 0, 0);
+                    }
+                }
+                __syncthreads();
+            };
+            constexpr int UN = kSlots;
+            const int nmain = nks - nks % UN;
+            for (int ks0 = 0; ks0 < nmain; ks0 += UN)
+                static_for<UN>([&](auto U) __attribute__((always_inline)) { cstep(U, ks0 + decltype(U)::value); });
+            static_for<UN - 1>([&](auto U) __attribute__((always_inline)) {
+                if (nmain + decltype(U)::value < nks) cstep(U, nmain + decltype(U)::value);
+            });
+
+            // ---- epilogue of the pass: logits and the rows' (max, sum exp) over this tile
+            if (cvalid) {
+#pragma unroll
+                for (int i = 0; i < MT; ++i) {
+                    const int m = m0 + i * 32 + lr;
+                    float mx = -INFINITY;
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const int v0 = tile * 32 + 8 * g + 4 * lh;
+                        const f32x4 z = {acc[i][4 * g], acc[i][4 * g + 1], acc[i][4 * g + 2], acc[i][4 * g + 3]};
+                        if (m < a.M) {
+                            float* dst = a.logits + (int64_t)m * a.ldz + v0;
+                            if (v0 + 3 < a.V) {
+                                *reinterpret_cast<f32x4*>(dst) = z;
+                            } else {
+#pragma unroll
+                                for (int q = 0; q < 4; ++q)
+                                    if (v0 + q < a.V) dst[q] = z[q];
+                            }
+                        }
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            if (v0 + q < a.V) mx = fmaxf(mx, z[q]);
+                    }
+                    float sm = 0.f;
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const int v0 = tile * 32 + 8 * g + 4 * lh;
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            if (v0 + q < a.V) sm += __expf(acc[i][4 * g + q] - mx);
+                    }
+                    const float m2 = __shfl_xor(mx, 32);
+                    const float s2 = __shfl_xor(sm, 32);
+                    lse_merge(mx, sm, m2, s2);
+                    lse_merge(run_m[i], run_s[i], mx, sm);
+                }
+            }
+        }
+        // one partial per (row, consumer wave): column b * kConsumers + wave of the partial array
+        if (lh == 0) {
+#pragma unroll
+            for (int i = 0; i < MT; ++i) {
+                const int m = m0 + i * 32 + lr;
+                if (m < a.M)
+                    a.part[(int64_t)m * a.G * kConsumers + b * kConsumers + wave] = make_float2(run_m[i], run_s[i]);
+            }
+        }
+    }
+}
+
 template <int MT>
 hipError_t launch_mt(const LmHeadArgs& a, dim3 grid, hipStream_t s) {
-    hipLaunchKernelGGL((lmhead_gemm_lse_kernel<MT, kNT>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((lmhead_gemm_lse_kernel<MT, kNT, kDepth>), grid, dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 
-int row_tiles_per_chunk(int M) {
-    if (M <= 0) return 1;
-    const int gy = (M + 255) / 256;
-    const int rows = (M + gy - 1) / gy;
-    return (rows + 15) / 16;
+template <int MT>
+hipError_t launch_pc(const LmHeadArgs& a, dim3 grid, hipStream_t s) {
+    hipLaunchKernelGGL((lmhead_pc_kernel<MT>), grid, dim3(kPcThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+// Up to 64 rows: the vocab-split kernel with ceil(M / 16) row tiles.  More:
+// the warp-specialised kernel on row chunks of up to 224 rows (seven 32-row
+// tiles: the most whose accumulators and load rings fit the register file).
+constexpr int kPcMaxRows = 224;
+bool small_rows(int M) { return M <= 64; }
+int row_tiles_small(int M) { return M <= 0 ? 1 : (M + 15) / 16; }
+int pc_chunks(int M) { return (M + kPcMaxRows - 1) / kPcMaxRows; }
+int pc_tiles(int M) {   // 32-row tiles per chunk
+    const int gy = pc_chunks(M);
+    return ((M + gy - 1) / gy + 31) / 32;
+}
+// workgroups along the vocabulary
+int lmhead_grid(int M, int V) {
+    if (small_rows(M)) {
+        const int tiles = (V + 15) / 16;
+        const int need = (tiles + 4 * kNT - 1) / (4 * kNT);
+        const int cap = row_tiles_small(M) <= 2 ? 1024 : 512;
+        return need < cap ? need : cap;
+    }
+    const int tiles = (V + 31) / 32;
+    const int need = (tiles + kConsumers - 1) / kConsumers;
+    const int cap = 256 / pc_chunks(M) > 0 ? 256 / pc_chunks(M) : 1;
+    return need < cap ? need : cap;
 }
 
 // One (max, sum) partial per row and vocabulary workgroup -> lse.
@@ -270,15 +541,8 @@ __global__ void __launch_bounds__(256) row_lse_kernel(const float* logits, int64
 
 }  // namespace
 
-int lmhead_grid_y(int M) { return (M + 255) / 256; }
-
-int lmhead_grid_x(int M, int V) {
-    const int mt = row_tiles_per_chunk(M);
-    const int tiles = (V + 15) / 16;
-    const int per_pass = 4 * kNT;
-    const int cap = mt <= 4 ? 1024 : (mt <= 8 ? 512 : 256);
-    const int need = (tiles + per_pass - 1) / per_pass;
-    return need < cap ? need : cap;
+int lmhead_partials(int M, int V) {
+    return small_rows(M) ? lmhead_grid(M, V) : lmhead_grid(M, V) * kConsumers;
 }
 
 hipError_t launch_lmhead(const uint16_t* hidden, const uint16_t* W, float* logits, int64_t ldz,
@@ -287,26 +551,25 @@ hipError_t launch_lmhead(const uint16_t* hidden, const uint16_t* W, float* logit
     LmHeadArgs a;
     a.hidden = hidden; a.W = W; a.logits = logits; a.part = lse_part; a.ldz = ldz;
     a.M = M; a.H = H; a.V = V;
-    a.tiles = (V + 15) / 16;
-    a.G = lmhead_grid_x(M, V);
-    const dim3 grid(a.G, lmhead_grid_y(M));
-    switch (row_tiles_per_chunk(M)) {
-        case 1: return launch_mt<1>(a, grid, s);
-        case 2: return launch_mt<2>(a, grid, s);
-        case 3: return launch_mt<3>(a, grid, s);
-        case 4: return launch_mt<4>(a, grid, s);
-        case 5: return launch_mt<5>(a, grid, s);
-        case 6: return launch_mt<6>(a, grid, s);
-        case 7: return launch_mt<7>(a, grid, s);
-        case 8: return launch_mt<8>(a, grid, s);
-        case 9: return launch_mt<9>(a, grid, s);
-        case 10: return launch_mt<10>(a, grid, s);
-        case 11: return launch_mt<11>(a, grid, s);
-        case 12: return launch_mt<12>(a, grid, s);
-        case 13: return launch_mt<13>(a, grid, s);
-        case 14: return launch_mt<14>(a, grid, s);
-        case 15: return launch_mt<15>(a, grid, s);
-        default: return launch_mt<16>(a, grid, s);
+    a.G = lmhead_grid(M, V);
+    if (small_rows(M)) {
+        a.tiles = (V + 15) / 16;
+        const dim3 grid(a.G, 1);
+        switch (row_tiles_small(M)) {
+            case 1: return launch_mt<1>(a, grid, s);
+            case 2: return launch_mt<2>(a, grid, s);
+            case 3: return launch_mt<3>(a, grid, s);
+            default: return launch_mt<4>(a, grid, s);
+        }
+    }
+    a.tiles = (V + 31) / 32;
+    const dim3 grid(a.G, pc_chunks(M));
+    switch (pc_tiles(M)) {
+        case 3: return launch_pc<3>(a, grid, s);
+        case 4: return launch_pc<4>(a, grid, s);
+        case 5: return launch_pc<5>(a, grid, s);
+        case 6: return launch_pc<6>(a, grid, s);
+        default: return launch_pc<7>(a, grid, s);
     }
 }
 

@@ -57,26 +57,50 @@ __device__ __forceinline__ int block_excl_scan(int v, int* wsum, int& total) {
 }
 
 // Slot-order the n unique entries of list[0..n) and write the first K to out
-// (empty entries fill the rest when n < K).
+// (empty entries fill the rest when n < K).  list[n] must be readable and hold
+// kEmptyEntry when n is odd (it is read in pairs and beats nothing).
 __device__ __forceinline__ void rank_place(const uint64_t* list, int n, int K, uint64_t* out) {
+    const ulonglong2* pairs = reinterpret_cast<const ulonglong2*>(list);
+    const int np = (n + 1) >> 1;
     for (int i = threadIdx.x; i < n; i += kThreads) {
         const uint64_t my = list[i];
         int rank = 0;
-        for (int j = 0; j < n; ++j) rank += (list[j] > my) ? 1 : 0;
+#pragma unroll 4
+        for (int j = 0; j < np; ++j) {
+            const ulonglong2 e = pairs[j];
+            rank += (e.x > my) ? 1 : 0;
+            rank += (e.y > my) ? 1 : 0;
+        }
         if (rank < K) out[rank] = my;
     }
     for (int i = n + threadIdx.x; i < K; i += kThreads) out[i] = kEmptyEntry;
+}
+
+// The 64 lanes' values sorted in descending order across the wave (bitonic
+// network over lane pairs); lane i returns the (i+1)-th largest.
+__device__ __forceinline__ uint32_t wave_sort_desc(uint32_t x) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int k = 2; k <= 64; k <<= 1) {
+#pragma unroll
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            const uint32_t y = (uint32_t)__shfl_xor((int)x, j);
+            const bool desc = (lane & k) == 0;
+            const bool lower = (lane & j) == 0;
+            x = (desc == lower) ? max(x, y) : min(x, y);
+        }
+    }
+    return x;
 }
 
 template <int PT>
 __global__ void __launch_bounds__(kThreads) topk_chunk_kernel(const float* __restrict__ logits, int64_t ldz,
                                                               int V, int K, int nchunks,
                                                               uint64_t* __restrict__ best) {
-    __shared__ uint32_t tmax[kThreads];
-    __shared__ uint64_t cand[kFastCap];
+    __shared__ uint32_t wtau[4];
+    __shared__ __attribute__((aligned(16))) uint64_t cand[kFastCap + 2];
     __shared__ uint32_t hist[256];
     __shared__ int wsum[4];
-    __shared__ uint32_t s_tau;
     __shared__ int s_digit, s_want;
 
     const int tid = threadIdx.x;
@@ -97,22 +121,18 @@ __global__ void __launch_bounds__(kThreads) topk_chunk_kernel(const float* __res
     }
     auto id_of = [&](int e) { return (uint32_t)(cbase + (e >> 2) * (4 * kThreads) + 4 * tid + (e & 3)); };
 
-    // ---- tau: K-th largest per-thread maximum (ties ranked by thread index)
+    // ---- tau: with q = ceil(K / 4), every wave has q lanes whose maximum is at
+    // least the q-th largest lane maximum of that wave, so at least 4q >= K keys
+    // of the chunk are >= the smallest of the four waves' q-th largest maxima.
     uint32_t mx = 0;
 #pragma unroll
     for (int e = 0; e < PT; ++e) mx = max(mx, key[e]);
-    tmax[tid] = mx;
+    const uint32_t sorted = wave_sort_desc(mx);
+    const int q = (K + 3) >> 2;
+    const uint32_t wq = (uint32_t)__builtin_amdgcn_readlane((int)sorted, q - 1);
+    if ((tid & 63) == 0) wtau[tid >> 6] = wq;
     __syncthreads();
-    {
-        int rank = 0;
-        for (int i = 0; i < kThreads; ++i) {
-            const uint32_t o = tmax[i];
-            rank += (o > mx || (o == mx && i < tid)) ? 1 : 0;
-        }
-        if (rank == K - 1) s_tau = mx;
-    }
-    __syncthreads();
-    const uint32_t tau = max(s_tau, 1u);   // key 0 marks positions past the row
+    const uint32_t tau = max(min(min(wtau[0], wtau[1]), min(wtau[2], wtau[3])), 1u);   // key 0: past the row
 
     int cnt = 0;
 #pragma unroll
@@ -125,6 +145,7 @@ __global__ void __launch_bounds__(kThreads) topk_chunk_kernel(const float* __res
 #pragma unroll
         for (int e = 0; e < PT; ++e)
             if (key[e] >= tau && p < kFastCap) cand[p++] = pack_entry(key[e], id_of(e));
+        if (tid == 0) cand[n] = kEmptyEntry;
         __syncthreads();
         rank_place(cand, n, K, out);
         return;
@@ -182,6 +203,7 @@ __global__ void __launch_bounds__(kThreads) topk_chunk_kernel(const float* __res
         }
         taken_base += tot;
     }
+    if (tid == 0) cand[K] = kEmptyEntry;
     __syncthreads();
     rank_place(cand, K, K, out);
 }
