@@ -257,182 +257,255 @@ __global__ void __launch_bounds__(kThreads) lmhead_gemm_lse_kernel(LmHeadArgs a)
         a.part[(int64_t)(m0 + tid) * a.G + b] = make_float2(run_m, run_s);
 }
 
-// ---------------------------------------------------------------- batched row tiles
-// More than 64 rows: a warp-specialised kernel.  Of the 8 waves of a
-// workgroup, waves 4..7 are producers: they only move data, W rows of the
-// pass and the hidden rows of the batch, from HBM and L2 into a 3-slot LDS
-// ring, through a register ring that keeps loads STEP_AHEAD 64-wide steps in
-// flight.  Waves 0..3 are consumers: they only read MFMA operands from LDS
-// and issue v_mfma_f32_32x32x16_bf16 (on gfx950 it sustains about 2.2
-// PFLOP/s with two accumulator chains; the 16x16x32 form reaches barely
-// half).  A producer's wait for its loads therefore never stalls an MFMA,
-// and memory and matrix work overlap instead of adding up.
-// Consumer w owns vocab tile w (32 rows) of every pass and all MT 32-row
-// tiles of the batch.  Operands: lane l covers row l % 32 and, in sub-step s
-// of a 64-wide step, reduction indices 64 ks + 32 (l / 32) + 8 s .. +7, the
-// same in A (W) and B (hidden).  Result register r of lane l is vocab entry
-// 8 (r / 4) + 4 (l / 32) + r % 4 of the tile for batch row l % 32, so a lane
-// stores four runs of four consecutive logits.
-// LDS rows are 128 bytes with the 16-byte chunk c of row r kept at chunk
-// c ^ swz(r), which makes the fragment reads conflict-free for 32- and
-// 64-bank LDS without padding.
-constexpr int kPcThreads = 512;
-constexpr int kConsumers = 4;
-constexpr int kSlots = 3;
-constexpr int kStepAhead = 3;
-
+// ---------------------------------------------------------------- batched rows (more than 64)
+// Four waves, one per SIMD, so that each wave may hold up to 512 registers:
+// wave w accumulates NV = 2 vocab tiles of 32 rows for all MT 32-row batch
+// tiles of its row chunk (2 MT 32x32 fp32 accumulators, in AGPRs), using
+// v_mfma_f32_32x32x16_bf16 (on gfx950 it sustains about 2.2 PFLOP/s with two
+// accumulator chains; the 16x16x32 form reaches barely half).
+//
+// Operands: lane l covers row l % 32 and, in sub-step s of a 64-wide step,
+// reduction indices 64 ks + 32 (l / 32) + 8 s .. +7, the same in A (W) and B
+// (hidden).  Result register r of lane l is vocab entry 8 (r / 4) + 4 (l / 32)
+// + r % 4 of the tile for batch row l % 32, so a lane stores four runs of four
+// consecutive logits.  LDS rows are 128 bytes with the 16-byte chunk c of row
+// r kept at chunk c ^ swz(r): the fragment reads are conflict-free without
+// padding.
+//
+// Every operand byte moves with buffer_load ... lds: each instruction fetches
+// eight whole 128-byte lines (eight lanes per row) and lands lane l's 16 bytes
+// at LDS byte 16 l of the instruction's 1 KB block; choosing which chunk of
+// its row each lane fetches makes that block the swizzled layout.  Rows past
+// the matrix, columns past H and the tiles a wave does not own in a short pass
+// get an offset past the described buffer range, so they read as zeros and
+// cost no memory traffic.
+//
+// LDS holds two hidden slots shared by the waves and three W slots per wave
+// (W runs two steps ahead).  One barrier per step: each wave first waits
+// until its own share of the hidden chunk of the step has landed.  The steps
+// of all passes of a workgroup form one stream, so the loads of the next pass
+// are in flight while a pass ends with its logits and (max, sum exp)
+// epilogue.  A pass normally gives each wave two tiles; the last pass of a
+// workgroup spreads what is left at one tile per wave when it can.
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
 
-template <int MT>
-__global__ void __launch_bounds__(kPcThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-lmhead_pc_kernel(LmHeadArgs a) {
-    constexpr int BN = kConsumers * 32;              // vocab rows per pass
-    constexpr int HR = MT * 32;                      // batch rows staged
-    constexpr int WP = BN * 8 / 256;                 // W pieces per producer thread per step
-    constexpr int HP = (HR * 8 + 255) / 256;         // hidden pieces per producer thread per step
-    __shared__ __attribute__((aligned(16))) uint8_t wsm[kSlots][BN][128];
-    __shared__ __attribute__((aligned(16))) uint8_t hsm[kSlots][HR][128];
+constexpr int kBufWord3 = 0x00020000;     // gfx9 buffer descriptor word 3 for raw dword access
+constexpr int kRowsWaves = 4;             // waves, and so (max, sum) partials, per workgroup
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+
+constexpr int kBig = 0x40000000;   // buffer offset past every described range (ranges stay < 2^29)
+
+__device__ __forceinline__ constexpr int waitcnt_vm(int n) {
+    // s_waitcnt immediate: vmcnt <= n; expcnt and lgkmcnt unconstrained
+    return (n & 0xf) | (0x7 << 4) | (0xf << 8) | ((n >> 4) << 14);
+}
+
+// Raw buffer descriptor (base, stride 0, size in bytes) in scalar registers.
+__device__ __forceinline__ u32x4 sbuf(const void* base, int64_t bytes) {
+    const uint64_t p = (uint64_t)base;
+    u32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((uint32_t)p);
+    r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32) & 0xffffu);
+    r[2] = __builtin_amdgcn_readfirstlane((uint32_t)(bytes < (1 << 29) ? bytes : (1 << 29)));
+    r[3] = kBufWord3;
+    return r;
+}
+
+// buffer_load_dwordx4 ... lds: lane l's 16 bytes at offset voff + soff land at LDS byte lds + 16 l.
+// Issued from inline assembly, so the compiler neither reorders it nor waits for it: every
+// wait for these loads is the explicit s_waitcnt vmcnt in the step loop.
+__device__ __forceinline__ void dma16(u32x4 rsrc, uint32_t lds, int voff, int soff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :
+                 : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+                 : "memory", "m0");
+}
+
+template <int MT, bool HFULL>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+lmhead_dma_kernel(LmHeadArgs a) {
+    constexpr int NV = 2;
+    constexpr int HR = MT * 32;                  // batch rows staged
+    constexpr int WR = NV * 32;                  // W rows of one wave per pass
+    constexpr int HSLOT = HR * 128;              // bytes of a hidden slot
+    constexpr int WSLOT = 4 * WR * 128;          // bytes of a W slot (all four waves)
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * HSLOT + 3 * WSLOT];
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)smem;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lr = lane & 31, lh = lane >> 5;
     const int b = blockIdx.x;
-    const int m0 = blockIdx.y * HR;                  // first batch row of this row chunk
+    const int m0 = blockIdx.y * HR;
     const int t_begin = (int)((int64_t)b * a.tiles / a.G);
     const int t_end = (int)((int64_t)(b + 1) * a.tiles / a.G);
     const int H = a.H;
     const int nks = (H + kBK - 1) / kBK;
     const int hchunks = H / 8;
 
-    // Both roles walk the same passes and steps, with one barrier per step plus one per pass,
-    // so their __syncthreads calls pair up.
-    if (wave >= kConsumers) {
-        // ================= producers: HBM / L2 -> registers -> LDS ring
-        const int ptid = tid - kConsumers * 64;      // 0..255
-        const int pc = ptid & 7;                     // 16-byte chunk of the pieces of this thread
-        const uint16_t* hsrc[HP];
-#pragma unroll
-        for (int q = 0; q < HP; ++q) {
-            const int row = (ptid + 256 * q) >> 3;
-            hsrc[q] = a.hidden + (int64_t)min(m0 + row, a.M - 1) * H;
-        }
-        for (int pt = t_begin; pt < t_end; pt += kConsumers) {
-            const bf16x8* wsrc[WP];
-#pragma unroll
-            for (int q = 0; q < WP; ++q) {
-                const int v = min(pt * 32 + ((ptid + 256 * q) >> 3), a.V - 1);
-                wsrc[q] = reinterpret_cast<const bf16x8*>(a.W + (int64_t)v * H);
-            }
-            auto load_step = [&](int ks, bf16x8 (&rw)[WP], bf16x8 (&rh)[HP]) __attribute__((always_inline)) {
-                const int chunk = min(ks * 8 + pc, hchunks - 1);
-#pragma unroll
-                for (int q = 0; q < WP; ++q) rw[q] = __builtin_nontemporal_load(wsrc[q] + chunk);
-#pragma unroll
-                for (int q = 0; q < HP; ++q) rh[q] = *reinterpret_cast<const bf16x8*>(hsrc[q] + chunk * 8);
-            };
-            auto store_step = [&](int slot, int ks, const bf16x8 (&rw)[WP], const bf16x8 (&rh)[HP])
-                __attribute__((always_inline)) {
-                const bool colok = ks * kBK + pc * 8 < H;    // columns past H are zero
-#pragma unroll
-                for (int q = 0; q < WP; ++q) {
-                    const int row = (ptid + 256 * q) >> 3;
-                    *reinterpret_cast<bf16x8*>(&wsm[slot][row][(pc ^ swz(row)) * 16]) = colok ? rw[q] : bf16x8{};
-                }
-#pragma unroll
-                for (int q = 0; q < HP; ++q) {
-                    const int row = (ptid + 256 * q) >> 3;
-                    const bool ok = colok && m0 + row < a.M;
-                    *reinterpret_cast<bf16x8*>(&hsm[slot][row][(pc ^ swz(row)) * 16]) = ok ? rh[q] : bf16x8{};
-                }
-            };
-            bf16x8 rw[kStepAhead][WP], rh[kStepAhead][HP];
-            // prologue: steps 0 .. kStepAhead-1 in flight, step 0 written to slot 0
-            static_for<kStepAhead>([&](auto D) __attribute__((always_inline)) {
-                load_step(decltype(D)::value, rw[decltype(D)::value], rh[decltype(D)::value]);
-            });
-            store_step(0, 0, rw[0], rh[0]);
-            __syncthreads();
-            // step ks: refill ring entry ks % kStepAhead with step ks + kStepAhead, then write
-            // step ks + 1 (loaded kStepAhead - 1 steps ago) into slot (ks + 1) % kSlots
-            auto pstep = [&](auto U, int ks) __attribute__((always_inline)) {
-                constexpr int u = decltype(U)::value;
-                load_step(ks + kStepAhead, rw[u % kStepAhead], rh[u % kStepAhead]);
-                store_step((u + 1) % kSlots, ks + 1, rw[(u + 1) % kStepAhead], rh[(u + 1) % kStepAhead]);
-                __syncthreads();
-            };
-            constexpr int UN = lcm3(kStepAhead, kSlots, 1);
-            const int nmain = nks - nks % UN;
-            for (int ks0 = 0; ks0 < nmain; ks0 += UN)
-                static_for<UN>([&](auto U) __attribute__((always_inline)) { pstep(U, ks0 + decltype(U)::value); });
-            static_for<UN - 1>([&](auto U) __attribute__((always_inline)) {
-                if (nmain + decltype(U)::value < nks) pstep(U, nmain + decltype(U)::value);
-            });
-        }
-    } else {
-        // ================= consumers: LDS -> MFMA, then the pass epilogue
-        float run_m[MT], run_s[MT];
-#pragma unroll
-        for (int i = 0; i < MT; ++i) { run_m[i] = 0.f; run_s[i] = 0.f; }
-        for (int pt = t_begin; pt < t_end; pt += kConsumers) {
-            const int tile = pt + wave;                  // this wave's vocab tile
-            const bool cvalid = tile < t_end;
-            f32x16 acc[MT];
-#pragma unroll
-            for (int i = 0; i < MT; ++i) acc[i] = f32x16{};
-            __syncthreads();   // pairs with the producers' prologue barrier
-            auto cstep = [&](auto U, int ks) __attribute__((always_inline)) {
-                constexpr int slot = decltype(U)::value % kSlots;
-                if (cvalid) {
-                    bf16x8 af[4];
-#pragma unroll
-                    for (int s = 0; s < 4; ++s) {
-                        const int r = wave * 32 + lr;
-                        af[s] = *reinterpret_cast<const bf16x8*>(&wsm[slot][r][((4 * lh + s) ^ swz(r)) * 16]);
-                    }
-#pragma unroll
-                    for (int i = 0; i < MT; ++i) {
-                        const int r = i * 32 + lr;
-                        bf16x8 hb[4];
-#pragma unroll
-                        for (int s = 0; s < 4; ++s)
-                            hb[s] = *reinterpret_cast<const bf16x8*>(&hsm[slot][r][((4 * lh + s) ^ swz(r)) * 16]);
-#pragma unroll
-                        for (int s = 0; s < 4; ++s)
-                            acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s], hb[s], acc[i], 0, 0, 0);
-                    }
-                }
-                __syncthreads();
-            };
-            constexpr int UN = kSlots;
-            const int nmain = nks - nks % UN;
-            for (int ks0 = 0; ks0 < nmain; ks0 += UN)
-                static_for<UN>([&](auto U) __attribute__((always_inline)) { cstep(U, ks0 + decltype(U)::value); });
-            static_for<UN - 1>([&](auto U) __attribute__((always_inline)) {
-                if (nmain + decltype(U)::value < nks) cstep(U, nmain + decltype(U)::value);
-            });
+    // pass plan: nfull passes of 4 NV tiles, then one pass over the rest (one tile per wave when it fits)
+    const int T = t_end - t_begin;
+    const int nfull = T / (4 * NV);
+    const int rest = T - nfull * 4 * NV;
+    const int npass = nfull + (rest > 0);
+    const int nv_last = rest <= 4 ? 1 : NV;
+    const int split = nv_last == 1 && rest > 0 ? nfull : npass;   // passes before the one-tile pass
+    auto pass_first = [&](int p) __attribute__((always_inline)) {
+        const int nv = p < nfull ? NV : nv_last;
+        return t_begin + p * 4 * NV + wave * nv;
+    };
+    auto pass_count = [&](int p) __attribute__((always_inline)) {
+        const int nv = p < nfull ? NV : nv_last;
+        const int c = t_end - pass_first(p);
+        return c < 0 ? 0 : (c < nv ? c : nv);
+    };
 
-            // ---- epilogue of the pass: logits and the rows' (max, sum exp) over this tile
-            if (cvalid) {
+    // ---- W: DMA instruction j of a step fills rows 8 j .. 8 j + 7 of the wave's part of a W slot
+    const int lrow = lane >> 3;                  // row within an instruction's 1 KB block
+    int wchunk[8];                               // logical chunk this lane fetches, per instruction
+#pragma unroll
+    for (int j = 0; j < 8; ++j) wchunk[j] = (lane & 7) ^ swz(8 * j + lrow);
+    u32x4 wbuf;
+    int wvoff[8];
+    int wp = 0, wks = 0;                         // W DMA cursor (pass, step); wp == npass: past the end
+    auto set_w = [&](int p) __attribute__((always_inline)) {
+        const int cnt = p < npass ? pass_count(p) : 0;
+        const int base = min(pass_first(p < npass ? p : npass - 1), a.tiles - 1) * 32;
+        const int64_t rest_bytes = (int64_t)(a.V - base) * H * 2;
+        const int64_t span = (int64_t)WR * H * 2;
+        wbuf = sbuf(a.W + (int64_t)base * H, rest_bytes < span ? rest_bytes : span);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int row = 8 * j + lrow;
+            wvoff[j] = (row >> 5) < cnt ? row * H * 2 + wchunk[j] * 16 : kBig;
+        }
+    };
+    auto issue_w = [&](uint32_t slot_lds) __attribute__((always_inline)) {
+        const uint32_t dst = slot_lds + wave * (WR * 128);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if constexpr (HFULL) {
+                dma16(wbuf, dst + j * 1024, wvoff[j], wks * (kBK * 2));
+            } else {
+                const bool ok = wks * 8 + wchunk[j] < hchunks;
+                dma16(wbuf, dst + j * 1024, ok ? wvoff[j] + wks * (kBK * 2) : kBig, 0);
+            }
+        }
+        if (++wks == nks) {
+            wks = 0;
+            ++wp;
+            set_w(wp < npass ? wp : npass);
+        }
+    };
+
+    // ---- hidden: instruction q of a wave fills rows (4 q + wave) * 8 .. + 7 of a hidden slot
+    const int mrows = min(a.M - m0, HR);
+    const u32x4 hbuf = sbuf(a.hidden + (int64_t)m0 * H, (int64_t)mrows * H * 2);
+    int hvoff[MT], hchunk[MT];
+#pragma unroll
+    for (int q = 0; q < MT; ++q) {
+        const int row = (4 * q + wave) * 8 + lrow;
+        hchunk[q] = (lane & 7) ^ swz(row);
+        hvoff[q] = row * H * 2 + hchunk[q] * 16;     // rows past the batch fall outside the range
+    }
+    int hks = 0;
+    auto issue_h = [&](uint32_t slot_lds) __attribute__((always_inline)) {
+#pragma unroll
+        for (int q = 0; q < MT; ++q) {
+            const uint32_t dst = slot_lds + (4 * q + wave) * 1024;
+            if constexpr (HFULL) {
+                dma16(hbuf, dst, hvoff[q], hks * (kBK * 2));
+            } else {
+                const bool ok = hks * 8 + hchunk[q] < hchunks;
+                dma16(hbuf, dst, ok ? hvoff[q] + hks * (kBK * 2) : kBig, 0);
+            }
+        }
+        if (++hks == nks) hks = 0;
+    };
+
+    // fragment byte offsets within a slot: row 32 t + lr (t = tile), chunk (4 lh + s) ^ swz(row);
+    // swz(32 t + lr) = swz(lr) ^ (4 (t & 1)), so two parities cover every tile
+    int foff[2][4];
+#pragma unroll
+    for (int par = 0; par < 2; ++par)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) foff[par][s] = lr * 128 + (((4 * lh + s) ^ swz(lr) ^ (4 * par)) * 16);
+
+    float run_m[MT], run_s[MT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i) { run_m[i] = 0.f; run_s[i] = 0.f; }
+
+    // ---- MFMAs of one step for NA tiles: W fragments first, then batch tiles, reads one tile ahead
+    auto mfma_step = [&](auto& acc, uint32_t hs, uint32_t ws) __attribute__((always_inline)) {
+        constexpr int NA = std::extent<std::remove_reference_t<decltype(acc)>>::value;
+        const uint8_t* hsp = smem + (hs - lds0);
+        const uint8_t* wsp = smem + (ws - lds0) + wave * (WR * 128);
+        bf16x8 wf[NA][4];
+#pragma unroll
+        for (int v = 0; v < NA; ++v)
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                wf[v][s] = *reinterpret_cast<const bf16x8*>(wsp + v * 4096 + foff[v & 1][s]);
+        bf16x8 hb[2][4];
+        auto read_frag = [&](int i, bf16x8 (&f)[4]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                f[s] = *reinterpret_cast<const bf16x8*>(hsp + i * 4096 + foff[i & 1][s]);
+        };
+        read_frag(0, hb[0]);
+        __builtin_amdgcn_sched_barrier(0);
+        static_for<MT>([&](auto I) __attribute__((always_inline)) {
+            constexpr int i = decltype(I)::value;
+            if constexpr (i + 1 < MT) read_frag(i + 1, hb[(i + 1) & 1]);
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int v = 0; v < NA; ++v)
+                    acc[v][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[v][s], hb[i & 1][s], acc[v][i], 0, 0, 0);
+            if constexpr (i + 1 < MT) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 4 * NA, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    };
+
+    // ---- pass epilogue: logits of the wave's tiles and their (max, sum exp) per batch row
+    auto epilogue = [&](auto& acc, int p) __attribute__((always_inline)) {
+        constexpr int NA = std::extent<std::remove_reference_t<decltype(acc)>>::value;
+        const int f = pass_first(p), cnt = pass_count(p);
+#pragma unroll
+        for (int v = 0; v < NA; ++v) {
+            if (v < cnt) {
+                const int tile = f + v;
 #pragma unroll
                 for (int i = 0; i < MT; ++i) {
                     const int m = m0 + i * 32 + lr;
+                    // one accumulator at a time into VGPRs, where it is used
+                    f32x16 z;
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) {
+                        float x;
+                        asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(x) : "a"(acc[v][i][j]));
+                        z[j] = x;
+                    }
                     float mx = -INFINITY;
 #pragma unroll
                     for (int g = 0; g < 4; ++g) {
                         const int v0 = tile * 32 + 8 * g + 4 * lh;
-                        const f32x4 z = {acc[i][4 * g], acc[i][4 * g + 1], acc[i][4 * g + 2], acc[i][4 * g + 3]};
+                        const f32x4 z4 = {z[4 * g], z[4 * g + 1], z[4 * g + 2], z[4 * g + 3]};
                         if (m < a.M) {
                             float* dst = a.logits + (int64_t)m * a.ldz + v0;
                             if (v0 + 3 < a.V) {
-                                *reinterpret_cast<f32x4*>(dst) = z;
+                                *reinterpret_cast<f32x4*>(dst) = z4;
                             } else {
 #pragma unroll
                                 for (int q = 0; q < 4; ++q)
-                                    if (v0 + q < a.V) dst[q] = z[q];
+                                    if (v0 + q < a.V) dst[q] = z4[q];
                             }
                         }
 #pragma unroll
                         for (int q = 0; q < 4; ++q)
-                            if (v0 + q < a.V) mx = fmaxf(mx, z[q]);
+                            if (v0 + q < a.V) mx = fmaxf(mx, z4[q]);
                     }
                     float sm = 0.f;
 #pragma unroll
@@ -440,23 +513,65 @@ lmhead_pc_kernel(LmHeadArgs a) {
                         const int v0 = tile * 32 + 8 * g + 4 * lh;
 #pragma unroll
                         for (int q = 0; q < 4; ++q)
-                            if (v0 + q < a.V) sm += __expf(acc[i][4 * g + q] - mx);
+                            if (v0 + q < a.V) sm += __expf(z[4 * g + q] - mx);
                     }
                     const float m2 = __shfl_xor(mx, 32);
                     const float s2 = __shfl_xor(sm, 32);
                     lse_merge(mx, sm, m2, s2);
                     lse_merge(run_m[i], run_s[i], mx, sm);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
-        }
-        // one partial per (row, consumer wave): column b * kConsumers + wave of the partial array
-        if (lh == 0) {
 #pragma unroll
-            for (int i = 0; i < MT; ++i) {
-                const int m = m0 + i * 32 + lr;
-                if (m < a.M)
-                    a.part[(int64_t)m * a.G * kConsumers + b * kConsumers + wave] = make_float2(run_m[i], run_s[i]);
+            for (int i = 0; i < MT; ++i) acc[v][i] = f32x16{};
+        }
+    };
+
+    if (npass > 0) {
+        const uint32_t hs_lds = lds0, ws_lds = lds0 + 2 * HSLOT;
+        // prologue: W 0, hidden 0, W 1, so that at every step exactly the 8 W loads of
+        // one later step were issued after the hidden chunk the step waits for
+        set_w(0);
+        issue_w(ws_lds);
+        issue_h(hs_lds);
+        issue_w(ws_lds + WSLOT);
+        int hsl = 0, wsl = 0;                    // slots of the current step (g % 2, g % 3)
+        auto run = [&](auto NA_, int p0, int p1) __attribute__((always_inline)) {
+            constexpr int NA = decltype(NA_)::value;
+            f32x16 acc[NA][MT];
+#pragma unroll
+            for (int v = 0; v < NA; ++v)
+#pragma unroll
+                for (int i = 0; i < MT; ++i) acc[v][i] = f32x16{};
+            for (int p = p0; p < p1; ++p) {
+                for (int ks = 0; ks < nks; ++ks) {
+                    // this wave's share of the hidden chunk of this step has landed (only the
+                    // W loads of the step after next may still be in flight); after the barrier
+                    // everyone's has, and the slots refilled below are no longer read
+                    __builtin_amdgcn_s_waitcnt(waitcnt_vm(8));
+                    asm volatile("" ::: "memory");
+                    __builtin_amdgcn_s_barrier();
+                    asm volatile("" ::: "memory");
+                    const int wnext = wsl == 0 ? 2 : wsl - 1;      // (g + 2) % 3
+                    issue_h(hs_lds + (hsl ^ 1) * HSLOT);
+                    issue_w(ws_lds + wnext * WSLOT);
+                    mfma_step(acc, hs_lds + hsl * HSLOT, ws_lds + wsl * WSLOT);
+                    hsl ^= 1;
+                    wsl = wsl == 2 ? 0 : wsl + 1;
+                }
+                epilogue(acc, p);
             }
+        };
+        run(std::integral_constant<int, NV>{}, 0, split);
+        if (split < npass) run(std::integral_constant<int, 1>{}, split, npass);
+        // the loads issued past the last step write LDS: let them land before the workgroup ends
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    }
+    if (lh == 0) {
+#pragma unroll
+        for (int i = 0; i < MT; ++i) {
+            const int m = m0 + i * 32 + lr;
+            if (m < a.M) a.part[(int64_t)m * a.G * kRowsWaves + b * kRowsWaves + wave] = make_float2(run_m[i], run_s[i]);
         }
     }
 }
@@ -468,20 +583,24 @@ hipError_t launch_mt(const LmHeadArgs& a, dim3 grid, hipStream_t s) {
 }
 
 template <int MT>
-hipError_t launch_pc(const LmHeadArgs& a, dim3 grid, hipStream_t s) {
-    hipLaunchKernelGGL((lmhead_pc_kernel<MT>), grid, dim3(kPcThreads), 0, s, a);
+hipError_t launch_rows(const LmHeadArgs& a, dim3 grid, hipStream_t s) {
+    if (a.H % kBK == 0)
+        hipLaunchKernelGGL((lmhead_dma_kernel<MT, true>), grid, dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((lmhead_dma_kernel<MT, false>), grid, dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
 // Up to 64 rows: the vocab-split kernel with ceil(M / 16) row tiles.  More:
-// the warp-specialised kernel on row chunks of up to 224 rows (seven 32-row
-// tiles: the most whose accumulators and load rings fit the register file).
-constexpr int kPcMaxRows = 224;
+// the batched kernel on row chunks of up to 256 rows (eight 32-row tiles: 256
+// AGPRs of accumulators and all 160 KB of LDS).
+constexpr int kMaxChunkRows = 256;
+constexpr int kRowsTilesPerPass = 4 * 2;
 bool small_rows(int M) { return M <= 64; }
 int row_tiles_small(int M) { return M <= 0 ? 1 : (M + 15) / 16; }
-int pc_chunks(int M) { return (M + kPcMaxRows - 1) / kPcMaxRows; }
-int pc_tiles(int M) {   // 32-row tiles per chunk
-    const int gy = pc_chunks(M);
+int row_chunks(int M) { return (M + kMaxChunkRows - 1) / kMaxChunkRows; }
+int chunk_tiles(int M) {   // 32-row tiles per chunk
+    const int gy = row_chunks(M);
     return ((M + gy - 1) / gy + 31) / 32;
 }
 // workgroups along the vocabulary
@@ -492,9 +611,10 @@ int lmhead_grid(int M, int V) {
         const int cap = row_tiles_small(M) <= 2 ? 1024 : 512;
         return need < cap ? need : cap;
     }
+    // one workgroup per CU (256 on MI355X) over all row chunks
     const int tiles = (V + 31) / 32;
-    const int need = (tiles + kConsumers - 1) / kConsumers;
-    const int cap = 256 / pc_chunks(M) > 0 ? 256 / pc_chunks(M) : 1;
+    const int need = (tiles + kRowsTilesPerPass - 1) / kRowsTilesPerPass;
+    const int cap = 256 / row_chunks(M) > 0 ? 256 / row_chunks(M) : 1;
     return need < cap ? need : cap;
 }
 
@@ -542,7 +662,7 @@ __global__ void __launch_bounds__(256) row_lse_kernel(const float* logits, int64
 }  // namespace
 
 int lmhead_partials(int M, int V) {
-    return small_rows(M) ? lmhead_grid(M, V) : lmhead_grid(M, V) * kConsumers;
+    return small_rows(M) ? lmhead_grid(M, V) : lmhead_grid(M, V) * kRowsWaves;
 }
 
 hipError_t launch_lmhead(const uint16_t* hidden, const uint16_t* W, float* logits, int64_t ldz,
@@ -563,13 +683,14 @@ hipError_t launch_lmhead(const uint16_t* hidden, const uint16_t* W, float* logit
         }
     }
     a.tiles = (V + 31) / 32;
-    const dim3 grid(a.G, pc_chunks(M));
-    switch (pc_tiles(M)) {
-        case 3: return launch_pc<3>(a, grid, s);
-        case 4: return launch_pc<4>(a, grid, s);
-        case 5: return launch_pc<5>(a, grid, s);
-        case 6: return launch_pc<6>(a, grid, s);
-        default: return launch_pc<7>(a, grid, s);
+    const dim3 grid(a.G, row_chunks(M));
+    switch (chunk_tiles(M)) {
+        case 3: return launch_rows<3>(a, grid, s);
+        case 4: return launch_rows<4>(a, grid, s);
+        case 5: return launch_rows<5>(a, grid, s);
+        case 6: return launch_rows<6>(a, grid, s);
+        case 7: return launch_rows<7>(a, grid, s);
+        default: return launch_rows<8>(a, grid, s);
     }
 }
 

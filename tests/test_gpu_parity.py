@@ -50,6 +50,9 @@ LMHEAD_CASES = [
     ("one_row", 1, 64, 17),                   # a single row and a single partial tile
     ("rows_224", 224, 256, 20000),            # the 224-row tile of the 4B batch
     ("rows_240", 240, 512, 33333),            # the 240-row tile of the 27B / pruned batches
+    ("rows_100_h200", 100, 200, 3001),        # batched rows, H not a multiple of 64 (column clamps)
+    ("rows_65_h8", 65, 8, 257),               # smallest batched case: one partial step, one tile tail
+    ("rows_480", 480, 192, 4133),             # two full 240-row chunks
 ]
 
 
