@@ -16,6 +16,7 @@ import os
 import sys
 import time
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 METRIC = "drafted blocks/sec (1 GPU) at Qwen3-4B shape; MFMA util + HBM GB/s vs peak"
@@ -136,6 +137,19 @@ def main():
     k2_bytes = z_bytes + M * 4 + M * K * (4 + 8 + 4)
     k2_gbs = k2_bytes / (k2_ms * 1e-3) / 1e9
 
+    # HBM traffic of the dominant kernel, from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    # record of this workload, valid only while the kernel sources are those it was taken on
+    traffic = None
+    rec_path = os.path.join(ROOT, "profiles", f"lmhead_dma_kernel__{shape.name}.traffic.json")
+    if os.path.exists(rec_path):
+        import hashlib
+        rec = json.load(open(rec_path))
+        h = hashlib.sha256(b"".join(open(os.path.join(ROOT, f), "rb").read() for f in rec["sources"])).hexdigest()
+        if h == rec["sources_sha256"]:
+            traffic = int(rec["traffic_bytes"])
+        else:
+            log("kernel sources changed since the traffic counters were taken: traffic = null")
+
     out = {
         "metric": METRIC,
         "value": round(blocks_per_s, 1),
@@ -153,9 +167,10 @@ def main():
                    "draft_vocab": Vd, "target_vocab": Vt, "top_k": K, "rank": r, "gated": shape.gated,
                    "pruned": shape.pruned, "walk": args.walk, "parallelism": "single GPU"},
         "rows_per_s": round(rows_per_s, 1),
-        "roofline": {"kernel": "lmhead_gemm_lse", "bound": "hbm", "achieved": round(k1_gbs, 1),
+        "roofline": {"kernel": "lmhead_dma_kernel" if M > 64 else "lmhead_gemm_lse_kernel", "bound": "hbm",
+                     "achieved": round(k1_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(k1_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": None, "bytes_per_launch": k1_bytes, "avg_launch_us": round(k1_ms * 1e3, 2),
+                     "traffic": traffic, "bytes_per_launch": k1_bytes, "avg_launch_us": round(k1_ms * 1e3, 2),
                      "mfma_tflops": round(k1_tflops, 1), "mfma_peak_tflops": BF16_MFMA_PEAK_TFLOPS,
                      "mfma_frac": round(k1_tflops / BF16_MFMA_PEAK_TFLOPS, 4)},
         "topk_pass": {"achieved_gbs": round(k2_gbs, 1), "frac": round(k2_gbs / HBM_PEAK_GBS, 4),
