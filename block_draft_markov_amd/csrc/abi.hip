@@ -90,7 +90,8 @@ int need(const void* p, int64_t count, const char* name) {
 
 struct Layout {
     int64_t ldz;
-    size_t logits, lse, part, best, cidx, ctok, unary, pair, total;
+    int64_t ldt;      // tile maxima stride (0: none, the Top-K reads every logit)
+    size_t logits, lse, part, tmax, best, cidx, ctok, unary, pair, total;
     int nparts;
 };
 
@@ -109,6 +110,8 @@ Layout layout(const dflash_dims* d) {
     l.logits = take((size_t)(M * l.ldz) * sizeof(float));
     l.lse = take((size_t)M * sizeof(float));
     l.part = take((size_t)(M * l.nparts) * sizeof(float2));
+    l.ldt = dflash::lmhead_has_tile_max(d->total_rows) ? (d->draft_vocab + 31) / 32 : 0;
+    l.tmax = take((size_t)(M * l.ldt) * sizeof(float));
     l.best = take((size_t)(M * p.nchunks * K) * sizeof(uint64_t));
     l.cidx = take((size_t)(M * K) * sizeof(int32_t));
     l.ctok = take((size_t)(M * K) * sizeof(int64_t));
@@ -170,13 +173,19 @@ int dflash_draft_block(const dflash_dims* d, const uint16_t* hidden, const uint1
     hipError_t e;
     float* logits = at<float>(ws, l.logits);
     float2* part = at<float2>(ws, l.part);
-    if ((e = dflash::launch_lmhead(hidden, lm_head, logits, l.ldz, part, d->total_rows, d->hidden,
+    float* tmax = l.ldt ? at<float>(ws, l.tmax) : nullptr;
+    if ((e = dflash::launch_lmhead(hidden, lm_head, logits, l.ldz, part, tmax, l.ldt, d->total_rows, d->hidden,
                                    d->draft_vocab, s)) != hipSuccess)
         return hip_fail(e, "lm_head launch");
-    if ((e = dflash::launch_topk(logits, l.ldz, nullptr, part, l.nparts, d2t, d->total_rows, d->draft_vocab,
-                                 d->top_k, at<uint64_t>(ws, l.best), at<int32_t>(ws, l.cidx),
-                                 at<int64_t>(ws, l.ctok), at<float>(ws, l.unary), s)) != hipSuccess)
-        return hip_fail(e, "top-k launch");
+    if (tmax)
+        e = dflash::launch_topk_tiles(logits, l.ldz, tmax, l.ldt, part, l.nparts, d2t, d->total_rows,
+                                      d->draft_vocab, d->top_k, at<int32_t>(ws, l.cidx), at<int64_t>(ws, l.ctok),
+                                      at<float>(ws, l.unary), s);
+    else
+        e = dflash::launch_topk(logits, l.ldz, nullptr, part, l.nparts, d2t, d->total_rows, d->draft_vocab,
+                                d->top_k, at<uint64_t>(ws, l.best), at<int32_t>(ws, l.cidx),
+                                at<int64_t>(ws, l.ctok), at<float>(ws, l.unary), s);
+    if (e != hipSuccess) return hip_fail(e, "top-k launch");
     if ((e = dflash::launch_pair_scores(at<int64_t>(ws, l.ctok), tables, gate_w, hidden, last_tok, row_offsets,
                                         d->num_requests, d->block_len, d->total_rows, d->hidden, d->target_vocab,
                                         d->top_k, d->rank, at<float>(ws, l.pair), s)) != hipSuccess)
@@ -206,7 +215,7 @@ int dflash_lm_head(const dflash_dims* d, const uint16_t* hidden, const uint16_t*
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
     float2* part = at<float2>(ws, l.part);
-    if ((e = dflash::launch_lmhead(hidden, lm_head, logits, ldz, part, d->total_rows, d->hidden, d->draft_vocab,
+    if ((e = dflash::launch_lmhead(hidden, lm_head, logits, ldz, part, nullptr, 0, d->total_rows, d->hidden, d->draft_vocab,
                                    s)) != hipSuccess)
         return hip_fail(e, "lm_head launch");
     if (lse && (e = dflash::launch_lse_combine(part, l.nparts, lse, d->total_rows, s)) != hipSuccess)

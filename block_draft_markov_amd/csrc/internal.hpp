@@ -8,11 +8,14 @@
 namespace dflash {
 
 // ---------------------------------------------------------------- part 1: lm_head GEMM
-// Vocabulary rows are handled in tiles of 16; a workgroup owns a contiguous
-// range of tiles and keeps one (max, sum exp) partial per row.
+// A workgroup owns a contiguous range of vocabulary tiles and keeps one
+// (max, sum exp) partial per row (per wave for more than 64 rows).
 int lmhead_partials(int M, int V);       // (max, sum exp) partials per row
+// For more than 64 rows the kernel can also store the maximum of every tile
+// of 32 logits of every row: tile_max [M][ldt], ldt >= ceil(V / 32).
+bool lmhead_has_tile_max(int M);
 hipError_t launch_lmhead(const uint16_t* hidden, const uint16_t* W, float* logits, int64_t ldz,
-                         float2* lse_part, int M, int H, int V, hipStream_t s);
+                         float2* lse_part, float* tile_max, int64_t ldt, int M, int H, int V, hipStream_t s);
 // lse[m] from the partials of row m.
 hipError_t launch_lse_combine(const float2* lse_part, int nparts, float* lse, int M, hipStream_t s);
 // lse[m] straight from logits.
@@ -28,6 +31,11 @@ TopkPlan topk_plan(int M, int V, int K);
 hipError_t launch_topk(const float* logits, int64_t ldz, const float* lse, const float2* lse_part,
                        int nparts, const int64_t* d2t, int M, int V, int K, uint64_t* chunk_best,
                        int32_t* cand_idx, int64_t* cand_tok, float* unary, hipStream_t s);
+// Top-K from the tile maxima of the lm_head kernel (one workgroup per row; rows
+// with heavy ties take an exact path over all their logits in the same launch).
+hipError_t launch_topk_tiles(const float* logits, int64_t ldz, const float* tile_max, int64_t ldt,
+                             const float2* lse_part, int nparts, const int64_t* d2t, int M, int V, int K,
+                             int32_t* cand_idx, int64_t* cand_tok, float* unary, hipStream_t s);
 
 // ---------------------------------------------------------------- parts 3 and 4: lattice
 hipError_t launch_pair_scores(const int64_t* cand_tok, const float* tables, const float* gate_w,

@@ -48,6 +48,8 @@ struct LmHeadArgs {
     const uint16_t* W;
     float* logits;
     float2* part;
+    float* tmax;     // per-tile maxima [M][ldt] or null (batched kernel only)
+    int64_t ldt;
     int64_t ldz;
     int M, H, V;
     int tiles;   // vocab tiles: ceil(V / 16) for the small-row kernel, ceil(V / 32) for the batched one
@@ -517,6 +519,7 @@ lmhead_dma_kernel(LmHeadArgs a) {
                     }
                     const float m2 = __shfl_xor(mx, 32);
                     const float s2 = __shfl_xor(sm, 32);
+                    if (a.tmax && lh == 0 && m < a.M) a.tmax[(int64_t)m * a.ldt + tile] = fmaxf(mx, m2);
                     lse_merge(mx, sm, m2, s2);
                     lse_merge(run_m[i], run_s[i], mx, sm);
                     __builtin_amdgcn_sched_barrier(0);
@@ -665,11 +668,14 @@ int lmhead_partials(int M, int V) {
     return small_rows(M) ? lmhead_grid(M, V) : lmhead_grid(M, V) * kRowsWaves;
 }
 
+bool lmhead_has_tile_max(int M) { return !small_rows(M); }
+
 hipError_t launch_lmhead(const uint16_t* hidden, const uint16_t* W, float* logits, int64_t ldz,
-                         float2* lse_part, int M, int H, int V, hipStream_t s) {
+                         float2* lse_part, float* tile_max, int64_t ldt, int M, int H, int V, hipStream_t s) {
     if (M <= 0) return hipSuccess;
     LmHeadArgs a;
     a.hidden = hidden; a.W = W; a.logits = logits; a.part = lse_part; a.ldz = ldz;
+    a.tmax = small_rows(M) ? nullptr : tile_max; a.ldt = ldt;
     a.M = M; a.H = H; a.V = V;
     a.G = lmhead_grid(M, V);
     if (small_rows(M)) {

@@ -33,6 +33,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kFastCap = 256;   // survivors ranked directly
+constexpr int kMaxTopK = 64;
 
 __device__ __forceinline__ int block_excl_scan(int v, int* wsum, int& total) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -93,21 +94,20 @@ __device__ __forceinline__ uint32_t wave_sort_desc(uint32_t x) {
     return x;
 }
 
-template <int PT>
-__global__ void __launch_bounds__(kThreads) topk_chunk_kernel(const float* __restrict__ logits, int64_t ldz,
-                                                              int V, int K, int nchunks,
-                                                              uint64_t* __restrict__ best) {
-    __shared__ uint32_t wtau[4];
-    __shared__ __attribute__((aligned(16))) uint64_t cand[kFastCap + 2];
-    __shared__ uint32_t hist[256];
-    __shared__ int wsum[4];
-    __shared__ int s_digit, s_want;
+struct ChunkShared {
+    uint32_t wtau[4];
+    __attribute__((aligned(16))) uint64_t cand[kFastCap + 2];
+    uint32_t hist[256];
+    int wsum[4];
+    int s_digit, s_want;
+};
 
+// The K best entries of logits [cbase, cbase + 256 PT) of `row` (ids < V), slot
+// ordered, into out[0..K) (global or LDS).  Called by all 256 threads; uses sh.
+template <int PT>
+__device__ __forceinline__ void chunk_select(const float* __restrict__ row, int cbase, int V, int K,
+                                             uint64_t* out, ChunkShared& sh) {
     const int tid = threadIdx.x;
-    const int c = blockIdx.x, m = blockIdx.y;
-    const int cbase = c * (kThreads * PT);
-    const float* row = logits + (int64_t)m * ldz;
-    uint64_t* out = best + ((int64_t)m * nchunks + c) * K;
 
     // ---- load PT logits per thread: element (j, q) has id cbase + j*1024 + 4*tid + q
     uint32_t key[PT];
@@ -130,50 +130,51 @@ __global__ void __launch_bounds__(kThreads) topk_chunk_kernel(const float* __res
     const uint32_t sorted = wave_sort_desc(mx);
     const int q = (K + 3) >> 2;
     const uint32_t wq = (uint32_t)__builtin_amdgcn_readlane((int)sorted, q - 1);
-    if ((tid & 63) == 0) wtau[tid >> 6] = wq;
+    if ((tid & 63) == 0) sh.wtau[tid >> 6] = wq;
     __syncthreads();
-    const uint32_t tau = max(min(min(wtau[0], wtau[1]), min(wtau[2], wtau[3])), 1u);   // key 0: past the row
+    const uint32_t tau = max(min(min(sh.wtau[0], sh.wtau[1]), min(sh.wtau[2], sh.wtau[3])), 1u);   // key 0: past the row
 
     int cnt = 0;
 #pragma unroll
     for (int e = 0; e < PT; ++e) cnt += (key[e] >= tau) ? 1 : 0;
     int n;
-    const int pos = block_excl_scan(cnt, wsum, n);
+    const int pos = block_excl_scan(cnt, sh.wsum, n);
 
     if (n <= kFastCap) {
         int p = pos;
 #pragma unroll
         for (int e = 0; e < PT; ++e)
-            if (key[e] >= tau && p < kFastCap) cand[p++] = pack_entry(key[e], id_of(e));
-        if (tid == 0) cand[n] = kEmptyEntry;
+            if (key[e] >= tau && p < kFastCap) sh.cand[p++] = pack_entry(key[e], id_of(e));
+        if (tid == 0) sh.cand[n] = kEmptyEntry;
         __syncthreads();
-        rank_place(cand, n, K, out);
+        rank_place(sh.cand, n, K, out);
+        __syncthreads();
         return;
     }
 
     // ---- fallback: exact K-th key by radix select on 8-bit digits
-    if (tid == 0) { s_digit = 0; s_want = 1; }
+    if (tid == 0) { sh.s_digit = 0; sh.s_want = 1; }
     uint32_t prefix = 0, pmask = 0;
     int want = K;
     for (int shift = 24; shift >= 0; shift -= 8) {
-        hist[tid] = 0;
+        sh.hist[tid] = 0;
         __syncthreads();
 #pragma unroll
         for (int e = 0; e < PT; ++e)
-            if (key[e] != 0u && (key[e] & pmask) == prefix) atomicAdd(&hist[(key[e] >> shift) & 255u], 1u);
+            if (key[e] != 0u && (key[e] & pmask) == prefix) atomicAdd(&sh.hist[(key[e] >> shift) & 255u], 1u);
         __syncthreads();
         if (tid == 0) {
             int cum = 0;
             for (int d = 255; d >= 0; --d) {
-                const int h = (int)hist[d];
-                if (cum + h >= want) { s_digit = d; s_want = want - cum; break; }
+                const int h = (int)sh.hist[d];
+                if (cum + h >= want) { sh.s_digit = d; sh.s_want = want - cum; break; }
                 cum += h;
             }
         }
         __syncthreads();
-        prefix |= (uint32_t)s_digit << shift;
+        prefix |= (uint32_t)sh.s_digit << shift;
         pmask |= 255u << shift;
-        want = s_want;
+        want = sh.s_want;
         __syncthreads();
     }
     const uint32_t T = prefix;   // the K-th largest key; `want` keys equal to T are taken
@@ -181,31 +182,42 @@ __global__ void __launch_bounds__(kThreads) topk_chunk_kernel(const float* __res
 #pragma unroll
     for (int e = 0; e < PT; ++e) ngt_t += (key[e] > T) ? 1 : 0;
     int ngt;
-    int p = block_excl_scan(ngt_t, wsum, ngt);
+    int p = block_excl_scan(ngt_t, sh.wsum, ngt);
 #pragma unroll
     for (int e = 0; e < PT; ++e)
-        if (key[e] > T && p < K) cand[p++] = pack_entry(key[e], id_of(e));
+        if (key[e] > T && p < K) sh.cand[p++] = pack_entry(key[e], id_of(e));
     // equal keys in id order: id order is (j, thread, q)
     int taken_base = 0;
 #pragma unroll
     for (int j = 0; j < PT / 4; ++j) {
         int neq = 0;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) neq += (key[4 * j + q] == T) ? 1 : 0;
+        for (int q2 = 0; q2 < 4; ++q2) neq += (key[4 * j + q2] == T) ? 1 : 0;
         int tot;
-        int ord = taken_base + block_excl_scan(neq, wsum, tot);
+        int ord = taken_base + block_excl_scan(neq, sh.wsum, tot);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            if (key[4 * j + q] == T) {
-                if (ord < want && ngt + ord < K) cand[ngt + ord] = pack_entry(T, id_of(4 * j + q));
+        for (int q2 = 0; q2 < 4; ++q2) {
+            if (key[4 * j + q2] == T) {
+                if (ord < want && ngt + ord < K) sh.cand[ngt + ord] = pack_entry(T, id_of(4 * j + q2));
                 ++ord;
             }
         }
         taken_base += tot;
     }
-    if (tid == 0) cand[K] = kEmptyEntry;
+    if (tid == 0) sh.cand[K] = kEmptyEntry;
     __syncthreads();
-    rank_place(cand, K, K, out);
+    rank_place(sh.cand, K, K, out);
+    __syncthreads();
+}
+
+template <int PT>
+__global__ void __launch_bounds__(kThreads) topk_chunk_kernel(const float* __restrict__ logits, int64_t ldz,
+                                                              int V, int K, int nchunks,
+                                                              uint64_t* __restrict__ best) {
+    __shared__ ChunkShared sh;
+    const int c = blockIdx.x, m = blockIdx.y;
+    chunk_select<PT>(logits + (int64_t)m * ldz, c * (kThreads * PT), V, K,
+                     best + ((int64_t)m * nchunks + c) * K, sh);
 }
 
 // Number of entries of the descending list y[0..n) that are > x (strict) or
@@ -228,22 +240,10 @@ __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2
     m = mn;
 }
 
-__global__ void __launch_bounds__(kThreads) topk_merge_kernel(const uint64_t* __restrict__ best, int nchunks, int K,
-                                                              const float* __restrict__ lse_in,
-                                                              const float2* __restrict__ lse_part, int nparts,
-                                                              const int64_t* __restrict__ d2t, int V,
-                                                              int32_t* __restrict__ cand_idx,
-                                                              int64_t* __restrict__ cand_tok,
-                                                              float* __restrict__ unary) {
-    extern __shared__ uint64_t lists[];   // 2 * nchunks * K entries
-    __shared__ float s_lse;
+// lse of row m from the (max, sum exp) partials, or the given value; broadcast to the block.
+__device__ __forceinline__ float row_lse_value(int m, const float* lse_in, const float2* lse_part, int nparts,
+                                              float* s_lse) {
     const int tid = threadIdx.x;
-    const int m = blockIdx.x;
-    uint64_t* a = lists;
-    uint64_t* b = lists + (int64_t)nchunks * K;
-    const uint64_t* src = best + (int64_t)m * nchunks * K;
-    for (int i = tid; i < nchunks * K; i += kThreads) a[i] = src[i];
-
     if (tid < 64) {
         float lse;
         if (lse_part) {
@@ -261,11 +261,16 @@ __global__ void __launch_bounds__(kThreads) topk_merge_kernel(const uint64_t* __
         } else {
             lse = lse_in[m];
         }
-        if (tid == 0) s_lse = lse;
+        if (tid == 0) *s_lse = lse;
     }
     __syncthreads();
+    return *s_lse;
+}
 
-    int nl = nchunks;
+// Merge nl slot-ordered lists of K entries held in LDS at a[0 .. nl K) (b is
+// scratch of the same size) pairwise into one; returns the buffer holding it.
+__device__ __forceinline__ uint64_t* merge_lists(uint64_t* a, uint64_t* b, int nl, int K) {
+    const int tid = threadIdx.x;
     while (nl > 1) {
         const int pairs = nl >> 1;
         // one thread per entry of both lists of every pair
@@ -285,10 +290,15 @@ __global__ void __launch_bounds__(kThreads) topk_merge_kernel(const uint64_t* __
         uint64_t* t = a; a = b; b = t;
         nl = pairs + (nl & 1);
     }
+    return a;
+}
 
-    const float lse = s_lse;
-    for (int k = tid; k < K; k += kThreads) {
-        const uint64_t e = a[k];
+// Slot k of row m from the final list: draft id, target id, unary score.
+__device__ __forceinline__ void write_row(const uint64_t* list, int m, int K, int V, float lse,
+                                          const int64_t* __restrict__ d2t, int32_t* __restrict__ cand_idx,
+                                          int64_t* __restrict__ cand_tok, float* __restrict__ unary) {
+    for (int k = threadIdx.x; k < K; k += kThreads) {
+        const uint64_t e = list[k];
         uint32_t id = entry_id(e);
         id = min(id, (uint32_t)(V - 1));   // an empty entry cannot reach the top K when K <= V
         const float z = key_to_float(entry_key(e));
@@ -297,6 +307,107 @@ __global__ void __launch_bounds__(kThreads) topk_merge_kernel(const uint64_t* __
         cand_tok[o] = d2t ? (int64_t)id + d2t[id] : (int64_t)id;
         unary[o] = z - lse;
     }
+}
+
+__global__ void __launch_bounds__(kThreads) topk_merge_kernel(const uint64_t* __restrict__ best, int nchunks, int K,
+                                                              const float* __restrict__ lse_in,
+                                                              const float2* __restrict__ lse_part, int nparts,
+                                                              const int64_t* __restrict__ d2t, int V,
+                                                              int32_t* __restrict__ cand_idx,
+                                                              int64_t* __restrict__ cand_tok,
+                                                              float* __restrict__ unary) {
+    extern __shared__ uint64_t lists[];   // 2 * nchunks * K entries
+    __shared__ float s_lse;
+    const int m = blockIdx.x;
+    const uint64_t* src = best + (int64_t)m * nchunks * K;
+    for (int i = threadIdx.x; i < nchunks * K; i += kThreads) lists[i] = src[i];
+    const float lse = row_lse_value(m, lse_in, lse_part, nparts, &s_lse);   // syncs the block
+    const uint64_t* fin = merge_lists(lists, lists + (int64_t)nchunks * K, nchunks, K);
+    write_row(fin, m, K, V, lse, d2t, cand_idx, cand_tok, unary);
+}
+
+// ---------------------------------------------------------------- from tile maxima
+// When the lm_head kernel also stored the maximum of every 32-logit tile of
+// every row, the top K of a row needs only a few of its tiles.  If tau is at
+// most the K-th largest tile maximum, at least K logits are >= tau, so every
+// member of the top K is >= tau and sits in a tile whose maximum is >= tau.
+// tau comes from the per-thread maxima of the tile maxima as in chunk_select;
+// the tiles it keeps (about K + 30 on smooth rows) are read, their logits
+// >= tau ranked.  A row with more than kSelCap such tiles or kCandCap such
+// logits (heavy ties) takes the exact path over all its logits instead.
+constexpr int kSelCap = 1024;
+constexpr int kCandCap = 512;
+
+__global__ void __launch_bounds__(kThreads) topk_tiles_kernel(const float* __restrict__ logits, int64_t ldz,
+                                                              const float* __restrict__ tmax, int64_t ldt,
+                                                              int tiles, int V, int K, int nchunks,
+                                                              const float2* __restrict__ lse_part, int nparts,
+                                                              const int64_t* __restrict__ d2t,
+                                                              int32_t* __restrict__ cand_idx,
+                                                              int64_t* __restrict__ cand_tok,
+                                                              float* __restrict__ unary) {
+    extern __shared__ uint64_t lists[];   // exact path: 2 * nchunks * K entries
+    __shared__ ChunkShared sh;
+    __shared__ int sel[kSelCap];
+    __shared__ __attribute__((aligned(16))) uint64_t cand[kCandCap + 2];
+    __shared__ uint64_t top[kMaxTopK];
+    __shared__ int s_nsel, s_ncand;
+    __shared__ float s_lse;
+    const int tid = threadIdx.x;
+    const int m = blockIdx.x;
+    const float* row = logits + (int64_t)m * ldz;
+    const float* trow = tmax + (int64_t)m * ldt;
+    const float lse = row_lse_value(m, nullptr, lse_part, nparts, &s_lse);   // syncs the block
+
+    // ---- tau from the tile maxima
+    uint32_t mx = 0;
+    for (int t = tid; t < tiles; t += kThreads) mx = max(mx, float_to_key(trow[t]));
+    const uint32_t sorted = wave_sort_desc(mx);
+    const int q = (K + 3) >> 2;
+    const uint32_t wq = (uint32_t)__builtin_amdgcn_readlane((int)sorted, q - 1);
+    if ((tid & 63) == 0) sh.wtau[tid >> 6] = wq;
+    if (tid == 0) { s_nsel = 0; s_ncand = 0; }
+    __syncthreads();
+    const uint32_t tau = max(min(min(sh.wtau[0], sh.wtau[1]), min(sh.wtau[2], sh.wtau[3])), 1u);
+
+    // ---- the tiles that may hold a member of the top K
+    for (int t = tid; t < tiles; t += kThreads) {
+        if (float_to_key(trow[t]) >= tau) {
+            const int i = atomicAdd(&s_nsel, 1);
+            if (i < kSelCap) sel[i] = t;
+        }
+    }
+    __syncthreads();
+    const int nsel = s_nsel;
+    bool exact = nsel > kSelCap;
+    if (!exact) {
+        // ---- their logits >= tau
+        for (int e = tid; e < nsel * 32; e += kThreads) {
+            const int v = sel[e >> 5] * 32 + (e & 31);
+            if (v < V) {
+                const uint32_t k = float_to_key(row[v]);
+                if (k >= tau) {
+                    const int i = atomicAdd(&s_ncand, 1);
+                    if (i < kCandCap) cand[i] = pack_entry(k, (uint32_t)v);
+                }
+            }
+        }
+        __syncthreads();
+        const int n = s_ncand;
+        exact = n > kCandCap;
+        if (!exact) {
+            if (tid == 0) cand[n] = kEmptyEntry;
+            __syncthreads();
+            rank_place(cand, n, K, top);
+            __syncthreads();
+            write_row(top, m, K, V, lse, d2t, cand_idx, cand_tok, unary);
+            return;
+        }
+    }
+    // ---- exact path: every chunk of the row, then the merge, all in this workgroup
+    for (int c = 0; c < nchunks; ++c) chunk_select<64>(row, c * (kThreads * 64), V, K, lists + (int64_t)c * K, sh);
+    const uint64_t* fin = merge_lists(lists, lists + (int64_t)nchunks * K, nchunks, K);
+    write_row(fin, m, K, V, lse, d2t, cand_idx, cand_tok, unary);
 }
 
 template <int PT>
@@ -347,6 +458,19 @@ hipError_t launch_topk(const float* logits, int64_t ldz, const float* lse, const
     const size_t lds = (size_t)2 * p.nchunks * K * sizeof(uint64_t);
     hipLaunchKernelGGL(topk_merge_kernel, dim3(M), dim3(kThreads), lds, s, chunk_best, p.nchunks, K, lse,
                        lse_part, nparts, d2t, V, cand_idx, cand_tok, unary);
+    return hipGetLastError();
+}
+
+int topk_tiles_chunks(int V) { return (V + kThreads * 64 - 1) / (kThreads * 64); }
+
+hipError_t launch_topk_tiles(const float* logits, int64_t ldz, const float* tile_max, int64_t ldt,
+                             const float2* lse_part, int nparts, const int64_t* d2t, int M, int V, int K,
+                             int32_t* cand_idx, int64_t* cand_tok, float* unary, hipStream_t s) {
+    if (M <= 0) return hipSuccess;
+    const int nchunks = topk_tiles_chunks(V);
+    const size_t lds = (size_t)2 * nchunks * K * sizeof(uint64_t);
+    hipLaunchKernelGGL(topk_tiles_kernel, dim3(M), dim3(kThreads), lds, s, logits, ldz, tile_max, ldt,
+                       (V + 31) / 32, V, K, nchunks, lse_part, nparts, d2t, cand_idx, cand_tok, unary);
     return hipGetLastError();
 }
 

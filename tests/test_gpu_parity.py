@@ -428,6 +428,28 @@ def test_end_to_end_pruned_ocr_sampled():
     _end_to_end(di.make_inputs(di.SHAPES["pruned_ocr"]), [2, 9])
 
 
+def _zero_hidden(inp):
+    inp.hidden[:] = 0    # bf16 +0: every logit is 0, the whole row ties
+    return inp
+
+
+@pytest.mark.parametrize("name,R,L,V,zero", [
+    ("batched_ragged_vocab", 20, 5, 5003, False),    # tile maxima path, partial last tile
+    ("batched_ties_all_tiles", 13, 7, 40000, True),  # every tile ties: more than 1024 tiles kept -> exact path
+    ("batched_ties_candidates", 17, 5, 3000, True),  # 94 tiles kept but 3000 tied logits -> exact path
+])
+def test_end_to_end_batched_tile_maxima_paths(name, R, L, V, zero):
+    """More than 64 rows: the Top-K reads only the tiles the lm_head tile maxima keep,
+    or all logits when ties keep too many; either way the same candidates as the
+    stand-alone Top-K over the full logits (checked bit for bit inside _end_to_end)."""
+    say(f"end-to-end {name}: R={R} L={L} V={V} zero_hidden={zero}")
+    sh = di.custom_shape(name, R=R, L=L, H=128, Vd=V, K=64, r=16, seed=70 + R)
+    inp = di.make_inputs(sh)
+    if zero:
+        inp = _zero_hidden(inp)
+    _end_to_end(inp, list(range(R)))
+
+
 def test_empty_batch_is_a_no_op():
     sh = di.custom_shape("empty", R=0, L=3, H=64, Vd=1024, K=8, r=4, seed=1)
     inp = di.make_inputs(sh)
