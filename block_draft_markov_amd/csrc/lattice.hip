@@ -9,15 +9,18 @@
 //   S_p[j][k] = g_p * <A[t_{p-1}[j]], B[t_p[k]]>,  S_0[0][k] = g_0 * <A[last], B[t_0[k]]>,
 //   g_p = sigmoid(w . h_p) when gated, else 1.
 // One workgroup per (position, request).  The K rows of A and of B it needs
-// are gathered from the fp32 tables in 64-wide slices of the rank, stored
-// transposed in LDS, and every thread accumulates a 4 x 4 block of S in a
-// fixed order over the rank.
+// are gathered whole (up to 256 rank elements at a time), every load in flight
+// at once, into LDS rows of 260 floats; thread (tj, tk) accumulates S[tj +
+// 16 x][tk + 16 y] for x, y < 4 in a fixed order over the rank (ascending), so
+// that its float4 reads of 16 consecutive B rows fall in distinct LDS banks.
 //
 // Walk (same commit: the greedy walk takes the best candidate after the token
-// before; the max-score walk is its Viterbi form): one wave per request, lane k
-// owns slot k.  Viterbi keeps delta(k) in a register; delta(j) reaches every
-// lane through readlane; back-pointers (lowest j at a tie) sit in LDS.  The
-// argmax of a position is a DPP max reduction and the lowest lane of a ballot.
+// before; the max-score walk is its Viterbi form): one 256-thread workgroup per
+// request stages up to eight positions of S and u in LDS at a time.  Viterbi:
+// thread (k, q) takes the best delta(j) + S[j][k] over j in its quarter q of
+// the slots (ascending, strict >), and the quarters are combined in order, so
+// the lowest j wins a tie; back-pointers stay in LDS.  Greedy: one wave, an
+// argmax per position (DPP max reduction, lowest lane of a ballot).
 
 #include "common.hpp"
 #include "internal.hpp"
@@ -30,8 +33,8 @@ namespace dflash {
 namespace {
 
 constexpr int kPairThreads = 256;
-constexpr int kSlice = 64;        // rank elements per LDS slice
-constexpr int kPad = 68;          // padded LDS row (floats): aligned float4 reads
+constexpr int kRankSlice = 256;   // rank elements staged per round
+constexpr int kPitch = kRankSlice + 4;   // LDS row pitch (floats): 16 consecutive rows hit distinct banks
 
 __device__ __forceinline__ void row_range(const int32_t* row_offsets, int req, int L, int M, int& a, int& n) {
     if (row_offsets) {
@@ -55,8 +58,8 @@ __global__ void __launch_bounds__(kPairThreads) pair_scores_kernel(
     const uint16_t* __restrict__ hidden, const int64_t* __restrict__ last_tok,
     const int32_t* __restrict__ row_offsets, int L, int M, int H, int Vt, int K, int r,
     float* __restrict__ pair) {
-    __shared__ __attribute__((aligned(16))) float As[kSlice][kPad];
-    __shared__ __attribute__((aligned(16))) float Bs[kSlice][kPad];
+    __shared__ __attribute__((aligned(16))) float As[64][kPitch];
+    __shared__ __attribute__((aligned(16))) float Bs[64][kPitch];
     __shared__ int64_t prev_row[64], cand_row[64];
     __shared__ float red[4];
 
@@ -67,18 +70,6 @@ __global__ void __launch_bounds__(kPairThreads) pair_scores_kernel(
     if (p >= n) return;
     const int m = a + p;
 
-    float g = 1.f;
-    if (gate_w) {
-        float part = 0.f;
-        const uint16_t* h = hidden + (int64_t)m * H;
-        for (int i = tid; i < H; i += kPairThreads) part += gate_w[i] * bf16_bits_to_float(h[i]);
-        part = wave_sum(part);
-        if ((tid & 63) == 0) red[tid >> 6] = part;
-        __syncthreads();
-        const float x = (red[0] + red[1]) + (red[2] + red[3]);
-        g = 1.f / (1.f + expf(-x));
-    }
-
     const int Jn = (p == 0) ? 1 : K;
     if (tid < 64) {
         const int64_t prev = (p == 0) ? last_tok[req] : (tid < K ? cand_tok[(int64_t)(m - 1) * K + tid] : 0);
@@ -86,7 +77,20 @@ __global__ void __launch_bounds__(kPairThreads) pair_scores_kernel(
         const int64_t cand = tid < K ? cand_tok[(int64_t)m * K + tid] : 0;
         cand_row[tid] = clamp_tok(cand, Vt) * r;
     }
+
+    float g = 1.f;
+    if (gate_w) {
+        float part = 0.f;
+        const uint16_t* h = hidden + (int64_t)m * H;
+        for (int i = tid; i < H; i += kPairThreads) part += gate_w[i] * bf16_bits_to_float(h[i]);
+        part = wave_sum(part);
+        if ((tid & 63) == 0) red[tid >> 6] = part;
+    }
     __syncthreads();
+    if (gate_w) {
+        const float x = (red[0] + red[1]) + (red[2] + red[3]);
+        g = 1.f / (1.f + expf(-x));
+    }
 
     const float* TA = tables;
     const float* TB = tables + (int64_t)Vt * r;
@@ -97,58 +101,49 @@ __global__ void __launch_bounds__(kPairThreads) pair_scores_kernel(
 #pragma unroll
         for (int y = 0; y < 4; ++y) acc[x][y] = 0.f;
 
-    // Gather of one 64-wide rank slice: row `row` of A (previous tokens) and of B
-    // (candidates), elements i0 .. i0+63.  With r % 4 == 0 the rows are 16-byte
-    // aligned and every thread loads 4 float4 of A and 4 of B; the next slice is
-    // in flight while the current one is multiplied.
+    // With r % 4 == 0 and 16-byte aligned tables every row is read as float4:
+    // float4 f of a slice is row f / 64 (A rows, then B rows), elements 4 (f % 64) ..
     const bool vec = (r & 3) == 0 && (reinterpret_cast<uintptr_t>(tables) & 15) == 0;
-    f32x4 ra[4], rb[4];
-    auto gather = [&](int i0) {
+    for (int i0 = 0; i0 < r; i0 += kRankSlice) {
+        const int w = min(kRankSlice, r - i0);        // rank elements of this slice
+        if (vec) {
+            f32x4 v[32];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int f4 = tid + i * kPairThreads;          // 0 .. 1023
-            const int row = f4 >> 4, c = (f4 & 15) * 4;     // 16 float4 per 64-wide row slice
-            f32x4 va = {0.f, 0.f, 0.f, 0.f}, vb = {0.f, 0.f, 0.f, 0.f};
-            if (vec) {
-                if (row < Jn && i0 + c < r) va = *reinterpret_cast<const f32x4*>(TA + prev_row[row] + i0 + c);
-                if (row < K && i0 + c < r) vb = *reinterpret_cast<const f32x4*>(TB + cand_row[row] + i0 + c);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    if (row < Jn && i0 + c + e < r) va[e] = TA[prev_row[row] + i0 + c + e];
-                    if (row < K && i0 + c + e < r) vb[e] = TB[cand_row[row] + i0 + c + e];
-                }
+            for (int i = 0; i < 32; ++i) {
+                const int f = tid + i * kPairThreads;       // 0 .. 8191
+                const int b = f >> 12, row = (f >> 6) & 63, c = (f & 63) * 4;
+                const bool ok = row < (b ? K : Jn) && c < w;
+                const float* src = (b ? TB + cand_row[row] : TA + prev_row[row]) + i0 + c;
+                v[i] = ok ? *reinterpret_cast<const f32x4*>(src) : f32x4{0.f, 0.f, 0.f, 0.f};
             }
-            ra[i] = va;
-            rb[i] = vb;
-        }
-    };
-    auto stash = [&]() {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int f4 = tid + i * kPairThreads;
-            const int row = f4 >> 4, c = (f4 & 15) * 4;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                As[c + e][row] = ra[i][e];
-                Bs[c + e][row] = rb[i][e];
+            for (int i = 0; i < 32; ++i) {
+                const int f = tid + i * kPairThreads;
+                const int b = f >> 12, row = (f >> 6) & 63, c = (f & 63) * 4;
+                *reinterpret_cast<f32x4*>(b ? &Bs[row][c] : &As[row][c]) = v[i];
+            }
+        } else {
+            for (int f = tid; f < 2 * 64 * kRankSlice; f += kPairThreads) {
+                const int b = f / (64 * kRankSlice), row = (f / kRankSlice) & 63, c = f % kRankSlice;
+                const bool ok = row < (b ? K : Jn) && c < w;
+                const float v = ok ? (b ? TB[cand_row[row] + i0 + c] : TA[prev_row[row] + i0 + c]) : 0.f;
+                if (b) Bs[row][c] = v; else As[row][c] = v;
             }
         }
-    };
-
-    gather(0);
-    for (int i0 = 0; i0 < r; i0 += kSlice) {
-        stash();
         __syncthreads();
-        if (i0 + kSlice < r) gather(i0 + kSlice);
-#pragma unroll 8
-        for (int ii = 0; ii < kSlice; ++ii) {
-            const f32x4 av = *reinterpret_cast<const f32x4*>(&As[ii][4 * tj]);
-            const f32x4 bv = *reinterpret_cast<const f32x4*>(&Bs[ii][4 * tk]);
+        const int w4 = (w + 3) >> 2;                  // elements past w are zero in both operands
+        for (int i4 = 0; i4 < w4; ++i4) {
+            f32x4 av[4], bv[4];
 #pragma unroll
-            for (int x = 0; x < 4; ++x)
+            for (int x = 0; x < 4; ++x) av[x] = *reinterpret_cast<const f32x4*>(&As[tj + 16 * x][4 * i4]);
 #pragma unroll
-                for (int y = 0; y < 4; ++y) acc[x][y] = fmaf(av[x], bv[y], acc[x][y]);
+            for (int y = 0; y < 4; ++y) bv[y] = *reinterpret_cast<const f32x4*>(&Bs[tk + 16 * y][4 * i4]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int x = 0; x < 4; ++x)
+#pragma unroll
+                    for (int y = 0; y < 4; ++y) acc[x][y] = fmaf(av[x][e], bv[y][e], acc[x][y]);
         }
         __syncthreads();
     }
@@ -156,96 +151,136 @@ __global__ void __launch_bounds__(kPairThreads) pair_scores_kernel(
     float* out = pair + (int64_t)m * K * K;
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
-        const int j = 4 * tj + x;
+        const int j = tj + 16 * x;
         if (j >= K) continue;
 #pragma unroll
         for (int y = 0; y < 4; ++y) {
-            const int k = 4 * tk + y;
+            const int k = tk + 16 * y;
             if (k < K) out[(int64_t)j * K + k] = (j < Jn) ? g * acc[x][y] : 0.f;
         }
     }
 }
 
-__global__ void __launch_bounds__(64) walk_kernel(const int64_t* __restrict__ cand_tok,
-                                                  const float* __restrict__ unary, const float* __restrict__ pair,
-                                                  const int32_t* __restrict__ row_offsets, int L, int M, int K,
-                                                  int walk, int64_t* __restrict__ tokens,
-                                                  float* __restrict__ scores, int32_t* __restrict__ slots) {
+constexpr int kWalkThreads = 256;
+constexpr int kWalkChunk = 8;     // positions of S and u staged in LDS at a time
+
+__global__ void __launch_bounds__(kWalkThreads) walk_kernel(const int64_t* __restrict__ cand_tok,
+                                                            const float* __restrict__ unary,
+                                                            const float* __restrict__ pair,
+                                                            const int32_t* __restrict__ row_offsets, int L, int M,
+                                                            int K, int walk, int64_t* __restrict__ tokens,
+                                                            float* __restrict__ scores,
+                                                            int32_t* __restrict__ slots) {
+    __shared__ __attribute__((aligned(16))) float Ss[kWalkChunk][64 * 64];
+    __shared__ float Us[kWalkChunk][64];
+    __shared__ float dcur[64];
+    __shared__ float qbest[4][64];
+    __shared__ int qarg[4][64];
     __shared__ uint8_t back[DFLASH_MAX_BLOCK_LEN][64];
     __shared__ int path[DFLASH_MAX_BLOCK_LEN];
-    const int req = blockIdx.x, lane = threadIdx.x;
+    __shared__ float s_score;
+    const int req = blockIdx.x, tid = threadIdx.x;
+    const int lane = tid & 63, q = tid >> 6;
     int a, n;
     row_range(row_offsets, req, L, M, a, n);
     if (n <= 0) {
-        if (lane == 0) scores[req] = 0.f;
+        if (tid == 0) scores[req] = 0.f;
         return;
     }
     const bool act = lane < K;
-    float score;
-    if (walk == DFLASH_WALK_VITERBI) {
-        float d = act ? unary[(int64_t)a * K + lane] + pair[(int64_t)a * K * K + lane] : -INFINITY;
-        // lane k needs column k of S_p (64 strided floats) and u_p[k]; the column of
-        // position p+1 is loaded while position p is folded in
-        float colA[64], colB[64];
-        float uA = 0.f, uB = 0.f;
-        auto load_col = [&](int p, float (&col)[64], float& u) {
-            const int64_t m = a + p;
-            const float* S = pair + m * K * K;
+    const int KK = K * K;
+    int prev = 0;            // greedy: slot of the previous position (wave 0)
+    float total = 0.f;       // greedy: running score (wave 0)
+    for (int c0 = 0; c0 < n; c0 += kWalkChunk) {
+        const int cn = min(kWalkChunk, n - c0);
+        // ---- stage S_p (K x K, row-major) and u_p of positions c0 .. c0 + cn
+        __syncthreads();
+        const float* src = pair + (int64_t)(a + c0) * KK;
+        if (K == 64 && (reinterpret_cast<uintptr_t>(pair) & 15) == 0) {
+            // all loads of the chunk in flight before the first LDS store
+            f32x4 v[kWalkChunk * 4];
 #pragma unroll
-            for (int j = 0; j < 64; ++j) col[j] = (j < K && act) ? S[j * K + lane] : 0.f;
-            u = act ? unary[m * K + lane] : 0.f;
-        };
-        auto fold = [&](int p, const float (&col)[64], float u) {
-            float best = -INFINITY;
-            int arg = 0;
+            for (int i = 0; i < kWalkChunk * 4; ++i) {
+                const int e = tid + i * kWalkThreads;
+                if (e < cn * 1024) v[i] = reinterpret_cast<const f32x4*>(src)[e];
+            }
 #pragma unroll
-            for (int j = 0; j < 64; ++j) {
-                if (j < K) {
-                    const float dj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(d), j));
-                    const float v = dj + col[j];
-                    if (v > best) { best = v; arg = j; }
+            for (int i = 0; i < kWalkChunk * 4; ++i) {
+                const int e = tid + i * kWalkThreads;
+                if (e < cn * 1024) reinterpret_cast<f32x4*>(&Ss[0][0])[e] = v[i];
+            }
+        } else {
+            for (int e = tid; e < cn * KK; e += kWalkThreads) {
+                const int pp = e / KK, o = e - pp * KK;
+                Ss[pp][(o / K) * 64 + (o % K)] = src[e];
+            }
+        }
+        for (int e = tid; e < cn * K; e += kWalkThreads) {
+            const int pp = e / K;
+            Us[pp][e - pp * K] = unary[(int64_t)(a + c0) * K + e];
+        }
+        __syncthreads();
+        for (int pp = 0; pp < cn; ++pp) {
+            const int p = c0 + pp;
+            if (walk == DFLASH_WALK_VITERBI) {
+                if (p == 0) {
+                    if (tid < 64) dcur[lane] = act ? Us[0][lane] + Ss[0][lane] : -INFINITY;
+                } else {
+                    // best over this thread's quarter of the previous slots, ascending j, strict >
+                    float best = -INFINITY;
+                    int arg = 16 * q;
+                    const int j0 = 16 * q, j1 = min(16 * q + 16, K);
+                    for (int j = j0; j < j1; ++j) {
+                        const float v = dcur[j] + Ss[pp][j * 64 + lane];
+                        if (v > best) { best = v; arg = j; }
+                    }
+                    qbest[q][lane] = best;
+                    qarg[q][lane] = arg;
+                    __syncthreads();
+                    if (tid < 64) {
+                        float b = qbest[0][lane];
+                        int ar = qarg[0][lane];
+#pragma unroll
+                        for (int qq = 1; qq < 4; ++qq)
+                            if (qbest[qq][lane] > b) { b = qbest[qq][lane]; ar = qarg[qq][lane]; }
+                        if (b == -INFINITY) ar = 0;   // nothing finite to extend: slot 0, as a scan from j = 0
+                        dcur[lane] = act ? Us[pp][lane] + b : -INFINITY;
+                        back[p][lane] = (uint8_t)min(ar, K - 1);
+                    }
+                }
+                __syncthreads();
+            } else if (tid < 64) {
+                const float v = act ? Us[pp][lane] + Ss[pp][prev * 64 + lane] : -INFINITY;
+                const float mx = wave_max(v);
+                const int c = min(lowest_lane(act && v == mx), K - 1);
+                total += mx;
+                if (lane == 0) path[p] = c;
+                prev = c;
+            }
+        }
+    }
+    if (tid < 64) {
+        float score;
+        if (walk == DFLASH_WALK_VITERBI) {
+            const float d = dcur[lane];
+            score = wave_max(d);
+            // NaN scores match no lane: fall back to slot 0 rather than index past the slots
+            const int last = min(lowest_lane(act && d == score), K - 1);
+            if (lane == 0) {
+                int c = last;
+                for (int p = n - 1; p >= 0; --p) {
+                    path[p] = c;
+                    if (p > 0) c = min((int)back[p][c], K - 1);
                 }
             }
-            d = act ? u + best : -INFINITY;
-            back[p][lane] = (uint8_t)arg;
-        };
-        if (n > 1) load_col(1, colA, uA);
-        for (int p = 1; p < n; p += 2) {
-            if (p + 1 < n) load_col(p + 1, colB, uB);
-            fold(p, colA, uA);
-            if (p + 1 < n) {
-                if (p + 2 < n) load_col(p + 2, colA, uA);
-                fold(p + 1, colB, uB);
-            }
+        } else {
+            score = total;
         }
-        score = wave_max(d);
-        // NaN scores match no lane: fall back to slot 0 rather than index past the slots
-        const int last = min(lowest_lane(act && d == score), K - 1);
-        __syncthreads();
-        if (lane == 0) {
-            int c = last;
-            for (int p = n - 1; p >= 0; --p) {
-                path[p] = c;
-                if (p > 0) c = min((int)back[p][c], K - 1);
-            }
-        }
-    } else {
-        int prev = 0;
-        float total = 0.f;
-        for (int p = 0; p < n; ++p) {
-            const int64_t m = a + p;
-            const float v = act ? unary[m * K + lane] + pair[(m * K + prev) * K + lane] : -INFINITY;
-            const float mx = wave_max(v);
-            const int c = min(lowest_lane(act && v == mx), K - 1);
-            total += mx;
-            if (lane == 0) path[p] = c;
-            prev = c;
-        }
-        score = total;
+        if (lane == 0) s_score = score;
     }
     __syncthreads();
-    if (lane == 0) scores[req] = score;
-    for (int p = lane; p < n; p += 64) {
+    if (tid == 0) scores[req] = s_score;
+    for (int p = tid; p < n; p += kWalkThreads) {
         const int c = path[p];
         tokens[a + p] = cand_tok[(int64_t)(a + p) * K + c];
         if (slots) slots[a + p] = c;
@@ -267,8 +302,8 @@ hipError_t launch_walk(const int64_t* cand_tok, const float* unary, const float*
                        int R, int L, int M, int K, int walk, int64_t* tokens, float* scores, int32_t* slots,
                        hipStream_t s) {
     if (R <= 0) return hipSuccess;
-    hipLaunchKernelGGL(walk_kernel, dim3(R), dim3(64), 0, s, cand_tok, unary, pair, row_offsets, L, M, K, walk,
-                       tokens, scores, slots);
+    hipLaunchKernelGGL(walk_kernel, dim3(R), dim3(kWalkThreads), 0, s, cand_tok, unary, pair, row_offsets, L, M, K,
+                       walk, tokens, scores, slots);
     return hipGetLastError();
 }
 
