@@ -72,14 +72,6 @@ constexpr int lcm3(int x, int y, int z) {
     return (x / gcd_c(x, y) * y) / gcd_c(x / gcd_c(x, y) * y, z) * z;
 }
 
-__device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
-    if (s2 == 0.f) return;
-    if (s == 0.f) { m = m2; s = s2; return; }
-    float mn = fmaxf(m, m2);
-    s = s * expf(m - mn) + s2 * expf(m2 - mn);
-    m = mn;
-}
-
 template <int MT, int NT, int DEPTH>
 __global__ void __launch_bounds__(kThreads) lmhead_gemm_lse_kernel(LmHeadArgs a) {
     constexpr int ROWS = MT * 16;
@@ -324,15 +316,19 @@ __device__ __forceinline__ void dma16(u32x4 rsrc, uint32_t lds, int voff, int so
                  : "memory", "m0");
 }
 
-template <int MT, bool HFULL>
+constexpr int kNV = 2;                    // vocab tiles per wave and pass
+constexpr int kWSlots = 3;                // W slots per wave: W runs kWSlots - 1 steps ahead
+template <int MT, bool HFULL, int SW = kWSlots>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 lmhead_dma_kernel(LmHeadArgs a) {
-    constexpr int NV = 2;
+    static_assert(SW >= 3, "the wait before each barrier assumes W is issued two or more steps ahead");
+    constexpr int NV = kNV;
+    constexpr int WJ = NV * 4;                   // W DMA instructions per wave and step
     constexpr int HR = MT * 32;                  // batch rows staged
     constexpr int WR = NV * 32;                  // W rows of one wave per pass
     constexpr int HSLOT = HR * 128;              // bytes of a hidden slot
     constexpr int WSLOT = 4 * WR * 128;          // bytes of a W slot (all four waves)
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * HSLOT + 3 * WSLOT];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * HSLOT + SW * WSLOT];
     const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)smem;
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -365,11 +361,11 @@ lmhead_dma_kernel(LmHeadArgs a) {
 
     // ---- W: DMA instruction j of a step fills rows 8 j .. 8 j + 7 of the wave's part of a W slot
     const int lrow = lane >> 3;                  // row within an instruction's 1 KB block
-    int wchunk[8];                               // logical chunk this lane fetches, per instruction
+    int wchunk[WJ];                               // logical chunk this lane fetches, per instruction
 #pragma unroll
-    for (int j = 0; j < 8; ++j) wchunk[j] = (lane & 7) ^ swz(8 * j + lrow);
+    for (int j = 0; j < WJ; ++j) wchunk[j] = (lane & 7) ^ swz(8 * j + lrow);
     u32x4 wbuf;
-    int wvoff[8];
+    int wvoff[WJ];
     int wp = 0, wks = 0;                         // W DMA cursor (pass, step); wp == npass: past the end
     auto set_w = [&](int p) __attribute__((always_inline)) {
         const int cnt = p < npass ? pass_count(p) : 0;
@@ -378,7 +374,7 @@ lmhead_dma_kernel(LmHeadArgs a) {
         const int64_t span = (int64_t)WR * H * 2;
         wbuf = sbuf(a.W + (int64_t)base * H, rest_bytes < span ? rest_bytes : span);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < WJ; ++j) {
             const int row = 8 * j + lrow;
             wvoff[j] = (row >> 5) < cnt ? row * H * 2 + wchunk[j] * 16 : kBig;
         }
@@ -386,7 +382,7 @@ lmhead_dma_kernel(LmHeadArgs a) {
     auto issue_w = [&](uint32_t slot_lds) __attribute__((always_inline)) {
         const uint32_t dst = slot_lds + wave * (WR * 128);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < WJ; ++j) {
             if constexpr (HFULL) {
                 dma16(wbuf, dst + j * 1024, wvoff[j], wks * (kBK * 2));
             } else {
@@ -535,10 +531,10 @@ lmhead_dma_kernel(LmHeadArgs a) {
         // prologue: W 0, hidden 0, W 1, so that at every step exactly the 8 W loads of
         // one later step were issued after the hidden chunk the step waits for
         set_w(0);
-        issue_w(ws_lds);
+        for (int i = 0; i + 2 < SW; ++i) issue_w(ws_lds + i * WSLOT);
         issue_h(hs_lds);
-        issue_w(ws_lds + WSLOT);
-        int hsl = 0, wsl = 0;                    // slots of the current step (g % 2, g % 3)
+        issue_w(ws_lds + (SW - 2) * WSLOT);
+        int hsl = 0, wsl = 0;                    // slots of the current step (g % 2, g % SW)
         auto run = [&](auto NA_, int p0, int p1) __attribute__((always_inline)) {
             constexpr int NA = decltype(NA_)::value;
             f32x16 acc[NA][MT];
@@ -551,16 +547,16 @@ lmhead_dma_kernel(LmHeadArgs a) {
                     // this wave's share of the hidden chunk of this step has landed (only the
                     // W loads of the step after next may still be in flight); after the barrier
                     // everyone's has, and the slots refilled below are no longer read
-                    __builtin_amdgcn_s_waitcnt(waitcnt_vm(8));
+                    __builtin_amdgcn_s_waitcnt(waitcnt_vm(WJ));
                     asm volatile("" ::: "memory");
                     __builtin_amdgcn_s_barrier();
                     asm volatile("" ::: "memory");
-                    const int wnext = wsl == 0 ? 2 : wsl - 1;      // (g + 2) % 3
+                    const int wnext = wsl == 0 ? SW - 1 : wsl - 1;      // (g + SW - 1) % SW
                     issue_h(hs_lds + (hsl ^ 1) * HSLOT);
                     issue_w(ws_lds + wnext * WSLOT);
                     mfma_step(acc, hs_lds + hsl * HSLOT, ws_lds + wsl * WSLOT);
                     hsl ^= 1;
-                    wsl = wsl == 2 ? 0 : wsl + 1;
+                    wsl = wsl == SW - 1 ? 0 : wsl + 1;
                 }
                 epilogue(acc, p);
             }
@@ -598,7 +594,7 @@ hipError_t launch_rows(const LmHeadArgs& a, dim3 grid, hipStream_t s) {
 // the batched kernel on row chunks of up to 256 rows (eight 32-row tiles: 256
 // AGPRs of accumulators and all 160 KB of LDS).
 constexpr int kMaxChunkRows = 256;
-constexpr int kRowsTilesPerPass = 4 * 2;
+constexpr int kRowsTilesPerPass = 4 * kNV;
 bool small_rows(int M) { return M <= 64; }
 int row_tiles_small(int M) { return M <= 0 ? 1 : (M + 15) / 16; }
 int row_chunks(int M) { return (M + kMaxChunkRows - 1) / kMaxChunkRows; }
@@ -621,21 +617,11 @@ int lmhead_grid(int M, int V) {
     return need < cap ? need : cap;
 }
 
-// One (max, sum) partial per row and vocabulary workgroup -> lse.
-__global__ void __launch_bounds__(64) lse_combine_kernel(const float2* part, int nparts, float* lse, int M) {
-    const int m = blockIdx.x;
-    const int lane = threadIdx.x;
-    float mx = 0.f, sm = 0.f;
-    for (int i = lane; i < nparts; i += 64) {
-        const float2 p = part[(int64_t)m * nparts + i];
-        lse_merge(mx, sm, p.x, p.y);
-    }
-    for (int o = 32; o > 0; o >>= 1) {
-        const float m2 = __shfl_xor(mx, o);
-        const float s2 = __shfl_xor(sm, o);
-        lse_merge(mx, sm, m2, s2);
-    }
-    if (lane == 0) lse[m] = mx + logf(sm);
+// One (max, sum) partial per row and vocabulary workgroup (or wave) -> lse.
+__global__ void __launch_bounds__(256) lse_combine_kernel(const float2* part, int nparts, float* lse, int M) {
+    __shared__ float2 red[4];
+    const float v = block_lse(part, blockIdx.x, nparts, red);
+    if (threadIdx.x == 0) lse[blockIdx.x] = v;
 }
 
 // lse of rows of given logits: a running (max, sum) per thread, merged in a fixed tree.
@@ -702,7 +688,7 @@ hipError_t launch_lmhead(const uint16_t* hidden, const uint16_t* W, float* logit
 
 hipError_t launch_lse_combine(const float2* lse_part, int nparts, float* lse, int M, hipStream_t s) {
     if (M <= 0) return hipSuccess;
-    hipLaunchKernelGGL(lse_combine_kernel, dim3(M), dim3(64), 0, s, lse_part, nparts, lse, M);
+    hipLaunchKernelGGL(lse_combine_kernel, dim3(M), dim3(256), 0, s, lse_part, nparts, lse, M);
     return hipGetLastError();
 }
 
