@@ -75,4 +75,44 @@ __device__ __forceinline__ float bf16_bits_to_float(uint16_t b) {
     return __uint_as_float(((uint32_t)b) << 16);
 }
 
+// Merge the (max, sum exp(x - max)) pair (m2, s2) into (m, s); s == 0 marks an empty pair.
+__device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
+    if (s2 == 0.f) return;
+    if (s == 0.f) { m = m2; s = s2; return; }
+    const float mn = fmaxf(m, m2);
+    s = s * expf(m - mn) + s2 * expf(m2 - mn);
+    m = mn;
+}
+
+// log-sum-exp of row m from its n (max, sum exp) partials part[m n .. m n + n),
+// for a 256-thread block (every thread returns it).  Each thread merges its
+// partials (eight loads in flight at a time), then the wave and the four waves
+// merge in a fixed order: one rounding sequence for every kernel that calls it.
+__device__ __forceinline__ float block_lse(const float2* __restrict__ part, int64_t m, int n, float2* red) {
+    const int tid = threadIdx.x;
+    const float2* row = part + m * n;
+    float mx = 0.f, sm = 0.f;
+    for (int base = 0; base < n; base += 256 * 8) {
+        float2 v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int idx = base + tid + 256 * i;
+            v[i] = idx < n ? row[idx] : make_float2(0.f, 0.f);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) lse_merge(mx, sm, v[i].x, v[i].y);
+    }
+    for (int o = 32; o > 0; o >>= 1) {
+        const float m2 = __shfl_xor(mx, o);
+        const float s2 = __shfl_xor(sm, o);
+        lse_merge(mx, sm, m2, s2);
+    }
+    __syncthreads();
+    if ((tid & 63) == 0) red[tid >> 6] = make_float2(mx, sm);
+    __syncthreads();
+    float a = 0.f, s = 0.f;
+    for (int w = 0; w < 4; ++w) lse_merge(a, s, red[w].x, red[w].y);
+    return a + logf(s);
+}
+
 }  // namespace dflash

@@ -162,7 +162,7 @@ __global__ void __launch_bounds__(kPairThreads) pair_scores_kernel(
 }
 
 constexpr int kWalkThreads = 256;
-constexpr int kWalkChunk = 8;     // positions of S and u staged in LDS at a time
+constexpr int kWalkChunk = 4;     // positions of S and u per LDS buffer; two buffers
 
 __global__ void __launch_bounds__(kWalkThreads) walk_kernel(const int64_t* __restrict__ cand_tok,
                                                             const float* __restrict__ unary,
@@ -171,11 +171,10 @@ __global__ void __launch_bounds__(kWalkThreads) walk_kernel(const int64_t* __res
                                                             int K, int walk, int64_t* __restrict__ tokens,
                                                             float* __restrict__ scores,
                                                             int32_t* __restrict__ slots) {
-    __shared__ __attribute__((aligned(16))) float Ss[kWalkChunk][64 * 64];
-    __shared__ float Us[kWalkChunk][64];
-    __shared__ float dcur[64];
-    __shared__ float qbest[4][64];
-    __shared__ int qarg[4][64];
+    __shared__ __attribute__((aligned(16))) float Ss[2][kWalkChunk][64 * 64];
+    __shared__ float Us[2][kWalkChunk][64];
+    __shared__ float qbest[2][4][64];
+    __shared__ int qarg[2][4][64];
     __shared__ uint8_t back[DFLASH_MAX_BLOCK_LEN][64];
     __shared__ int path[DFLASH_MAX_BLOCK_LEN];
     __shared__ float s_score;
@@ -189,68 +188,85 @@ __global__ void __launch_bounds__(kWalkThreads) walk_kernel(const int64_t* __res
     }
     const bool act = lane < K;
     const int KK = K * K;
+    const bool vec = K == 64 && (reinterpret_cast<uintptr_t>(pair) & 15) == 0;
+
+    // Staging of positions c0 .. c0 + cn into buffer `buf`.  With K = 64 every thread
+    // moves 16 float4 of S (one chunk = 4 x 16 KB): the loads of chunk c + 1 are issued
+    // before chunk c is walked and stored after it.
+    f32x4 sv[kWalkChunk * 4];
+    float uv = 0.f;
+    auto load_chunk = [&](int c0) {
+        const int cn = min(kWalkChunk, n - c0);
+        const f32x4* src = reinterpret_cast<const f32x4*>(pair + (int64_t)(a + c0) * KK);
+#pragma unroll
+        for (int i = 0; i < kWalkChunk * 4; ++i) {
+            const int e = tid + i * kWalkThreads;
+            if (e < cn * 1024) sv[i] = src[e];
+        }
+        uv = tid < cn * K ? unary[(int64_t)(a + c0) * K + tid] : 0.f;
+    };
+    auto store_chunk = [&](int c0, int buf) {
+        const int cn = min(kWalkChunk, n - c0);
+#pragma unroll
+        for (int i = 0; i < kWalkChunk * 4; ++i) {
+            const int e = tid + i * kWalkThreads;
+            if (e < cn * 1024) reinterpret_cast<f32x4*>(&Ss[buf][0][0])[e] = sv[i];
+        }
+        if (tid < cn * K) Us[buf][tid / K][tid % K] = uv;
+    };
+    auto stage_generic = [&](int c0, int buf) {
+        const int cn = min(kWalkChunk, n - c0);
+        const float* src = pair + (int64_t)(a + c0) * KK;
+        for (int e = tid; e < cn * KK; e += kWalkThreads) {
+            const int pp = e / KK, o = e - pp * KK;
+            Ss[buf][pp][(o / K) * 64 + (o % K)] = src[e];
+        }
+        for (int e = tid; e < cn * K; e += kWalkThreads) Us[buf][e / K][e % K] = unary[(int64_t)(a + c0) * K + e];
+    };
+
+    if (vec) { load_chunk(0); store_chunk(0, 0); } else { stage_generic(0, 0); }
+    __syncthreads();
+
+    // Viterbi: every wave keeps delta of the previous position in lane k (d), reads
+    // delta(j) by readlane, takes the best over its quarter j in [16 q, 16 q + 16),
+    // and after one barrier combines the four quarters in order (strict >).
+    float d = -INFINITY;
     int prev = 0;            // greedy: slot of the previous position (wave 0)
     float total = 0.f;       // greedy: running score (wave 0)
-    for (int c0 = 0; c0 < n; c0 += kWalkChunk) {
+    int par = 0;             // parity of the qbest buffers
+    for (int c0 = 0, buf = 0; c0 < n; c0 += kWalkChunk, buf ^= 1) {
         const int cn = min(kWalkChunk, n - c0);
-        // ---- stage S_p (K x K, row-major) and u_p of positions c0 .. c0 + cn
-        __syncthreads();
-        const float* src = pair + (int64_t)(a + c0) * KK;
-        if (K == 64 && (reinterpret_cast<uintptr_t>(pair) & 15) == 0) {
-            // all loads of the chunk in flight before the first LDS store
-            f32x4 v[kWalkChunk * 4];
-#pragma unroll
-            for (int i = 0; i < kWalkChunk * 4; ++i) {
-                const int e = tid + i * kWalkThreads;
-                if (e < cn * 1024) v[i] = reinterpret_cast<const f32x4*>(src)[e];
-            }
-#pragma unroll
-            for (int i = 0; i < kWalkChunk * 4; ++i) {
-                const int e = tid + i * kWalkThreads;
-                if (e < cn * 1024) reinterpret_cast<f32x4*>(&Ss[0][0])[e] = v[i];
-            }
-        } else {
-            for (int e = tid; e < cn * KK; e += kWalkThreads) {
-                const int pp = e / KK, o = e - pp * KK;
-                Ss[pp][(o / K) * 64 + (o % K)] = src[e];
-            }
-        }
-        for (int e = tid; e < cn * K; e += kWalkThreads) {
-            const int pp = e / K;
-            Us[pp][e - pp * K] = unary[(int64_t)(a + c0) * K + e];
-        }
-        __syncthreads();
+        const bool more = c0 + kWalkChunk < n;
+        if (more && vec) load_chunk(c0 + kWalkChunk);
         for (int pp = 0; pp < cn; ++pp) {
             const int p = c0 + pp;
             if (walk == DFLASH_WALK_VITERBI) {
                 if (p == 0) {
-                    if (tid < 64) dcur[lane] = act ? Us[0][lane] + Ss[0][lane] : -INFINITY;
+                    d = act ? Us[buf][0][lane] + Ss[buf][0][lane] : -INFINITY;
                 } else {
-                    // best over this thread's quarter of the previous slots, ascending j, strict >
                     float best = -INFINITY;
                     int arg = 16 * q;
                     const int j0 = 16 * q, j1 = min(16 * q + 16, K);
                     for (int j = j0; j < j1; ++j) {
-                        const float v = dcur[j] + Ss[pp][j * 64 + lane];
+                        const float dj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(d), j));
+                        const float v = dj + Ss[buf][pp][j * 64 + lane];
                         if (v > best) { best = v; arg = j; }
                     }
-                    qbest[q][lane] = best;
-                    qarg[q][lane] = arg;
+                    qbest[par][q][lane] = best;
+                    qarg[par][q][lane] = arg;
                     __syncthreads();
-                    if (tid < 64) {
-                        float b = qbest[0][lane];
-                        int ar = qarg[0][lane];
+                    float bb = qbest[par][0][lane];
+                    int ar = qarg[par][0][lane];
 #pragma unroll
-                        for (int qq = 1; qq < 4; ++qq)
-                            if (qbest[qq][lane] > b) { b = qbest[qq][lane]; ar = qarg[qq][lane]; }
-                        if (b == -INFINITY) ar = 0;   // nothing finite to extend: slot 0, as a scan from j = 0
-                        dcur[lane] = act ? Us[pp][lane] + b : -INFINITY;
-                        back[p][lane] = (uint8_t)min(ar, K - 1);
-                    }
+                    for (int qq = 1; qq < 4; ++qq)
+                        if (qbest[par][qq][lane] > bb) { bb = qbest[par][qq][lane]; ar = qarg[par][qq][lane]; }
+                    if (bb == -INFINITY) ar = 0;   // nothing finite to extend: slot 0, as a scan from j = 0
+                    d = act ? Us[buf][pp][lane] + bb : -INFINITY;
+                    if (q == 0) back[p][lane] = (uint8_t)min(ar, K - 1);
+                    par ^= 1;
                 }
-                __syncthreads();
             } else if (tid < 64) {
-                const float v = act ? Us[pp][lane] + Ss[pp][prev * 64 + lane] : -INFINITY;
+                const float v = act ? Us[buf][pp][lane] + Ss[buf][pp][prev * 64 + lane] : -INFINITY;
                 const float mx = wave_max(v);
                 const int c = min(lowest_lane(act && v == mx), K - 1);
                 total += mx;
@@ -258,11 +274,15 @@ __global__ void __launch_bounds__(kWalkThreads) walk_kernel(const int64_t* __res
                 prev = c;
             }
         }
+        if (more) {
+            __syncthreads();    // everyone is done with buffer buf ^ 1 (walked two chunks ago)
+            if (vec) store_chunk(c0 + kWalkChunk, buf ^ 1); else stage_generic(c0 + kWalkChunk, buf ^ 1);
+            __syncthreads();
+        }
     }
     if (tid < 64) {
         float score;
         if (walk == DFLASH_WALK_VITERBI) {
-            const float d = dcur[lane];
             score = wave_max(d);
             // NaN scores match no lane: fall back to slot 0 rather than index past the slots
             const int last = min(lowest_lane(act && d == score), K - 1);

@@ -232,39 +232,11 @@ __device__ __forceinline__ int count_better(const uint64_t* y, int n, uint64_t x
     return lo;
 }
 
-__device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
-    if (s2 == 0.f) return;
-    if (s == 0.f) { m = m2; s = s2; return; }
-    const float mn = fmaxf(m, m2);
-    s = s * expf(m - mn) + s2 * expf(m2 - mn);
-    m = mn;
-}
-
-// lse of row m from the (max, sum exp) partials, or the given value; broadcast to the block.
+// lse of row m from the (max, sum exp) partials, or the given value; the same for every thread.
 __device__ __forceinline__ float row_lse_value(int m, const float* lse_in, const float2* lse_part, int nparts,
-                                              float* s_lse) {
-    const int tid = threadIdx.x;
-    if (tid < 64) {
-        float lse;
-        if (lse_part) {
-            float mx = 0.f, sm = 0.f;
-            for (int i = tid; i < nparts; i += 64) {
-                const float2 pp = lse_part[(int64_t)m * nparts + i];
-                lse_merge(mx, sm, pp.x, pp.y);
-            }
-            for (int o = 32; o > 0; o >>= 1) {
-                const float m2 = __shfl_xor(mx, o);
-                const float s2 = __shfl_xor(sm, o);
-                lse_merge(mx, sm, m2, s2);
-            }
-            lse = mx + logf(sm);
-        } else {
-            lse = lse_in[m];
-        }
-        if (tid == 0) *s_lse = lse;
-    }
-    __syncthreads();
-    return *s_lse;
+                                              float2* red) {
+    if (lse_part) return block_lse(lse_part, m, nparts, red);
+    return lse_in[m];
 }
 
 // Merge nl slot-ordered lists of K entries held in LDS at a[0 .. nl K) (b is
@@ -317,11 +289,12 @@ __global__ void __launch_bounds__(kThreads) topk_merge_kernel(const uint64_t* __
                                                               int64_t* __restrict__ cand_tok,
                                                               float* __restrict__ unary) {
     extern __shared__ uint64_t lists[];   // 2 * nchunks * K entries
-    __shared__ float s_lse;
+    __shared__ float2 red[4];
     const int m = blockIdx.x;
     const uint64_t* src = best + (int64_t)m * nchunks * K;
     for (int i = threadIdx.x; i < nchunks * K; i += kThreads) lists[i] = src[i];
-    const float lse = row_lse_value(m, lse_in, lse_part, nparts, &s_lse);   // syncs the block
+    const float lse = row_lse_value(m, lse_in, lse_part, nparts, red);
+    __syncthreads();
     const uint64_t* fin = merge_lists(lists, lists + (int64_t)nchunks * K, nchunks, K);
     write_row(fin, m, K, V, lse, d2t, cand_idx, cand_tok, unary);
 }
@@ -337,6 +310,7 @@ __global__ void __launch_bounds__(kThreads) topk_merge_kernel(const uint64_t* __
 // logits (heavy ties) takes the exact path over all its logits instead.
 constexpr int kSelCap = 1024;
 constexpr int kCandCap = 512;
+constexpr int kTileCap = 8192;   // tile-maxima keys kept in LDS (32 KB); longer rows re-read them
 
 __global__ void __launch_bounds__(kThreads) topk_tiles_kernel(const float* __restrict__ logits, int64_t ldz,
                                                               const float* __restrict__ tmax, int64_t ldt,
@@ -348,20 +322,41 @@ __global__ void __launch_bounds__(kThreads) topk_tiles_kernel(const float* __res
                                                               float* __restrict__ unary) {
     extern __shared__ uint64_t lists[];   // exact path: 2 * nchunks * K entries
     __shared__ ChunkShared sh;
+    __shared__ uint32_t tkey[kTileCap];   // keys of the tile maxima (rows of at most kTileCap tiles)
     __shared__ int sel[kSelCap];
     __shared__ __attribute__((aligned(16))) uint64_t cand[kCandCap + 2];
     __shared__ uint64_t top[kMaxTopK];
     __shared__ int s_nsel, s_ncand;
-    __shared__ float s_lse;
+    __shared__ float2 red[4];
     const int tid = threadIdx.x;
     const int m = blockIdx.x;
     const float* row = logits + (int64_t)m * ldz;
     const float* trow = tmax + (int64_t)m * ldt;
-    const float lse = row_lse_value(m, nullptr, lse_part, nparts, &s_lse);   // syncs the block
+    const bool staged = tiles <= kTileCap;
+
+    // ---- the first kTileCap tile maxima are loaded before the lse partials, so that both
+    // sets of loads are in flight together; rows with more tiles loop over the rest
+    constexpr int kTPT = kTileCap / kThreads;   // tile maxima per thread in the first round
+    float tv[kTPT];
+#pragma unroll
+    for (int i = 0; i < kTPT; ++i) {
+        const int t = tid + kThreads * i;
+        tv[i] = t < tiles ? trow[t] : 0.f;
+    }
+    const float lse = block_lse(lse_part, m, nparts, red);
 
     // ---- tau from the tile maxima
     uint32_t mx = 0;
-    for (int t = tid; t < tiles; t += kThreads) mx = max(mx, float_to_key(trow[t]));
+#pragma unroll
+    for (int i = 0; i < kTPT; ++i) {
+        const int t = tid + kThreads * i;
+        if (t < tiles) {
+            const uint32_t k = float_to_key(tv[i]);
+            mx = max(mx, k);
+            tkey[t] = k;
+        }
+    }
+    for (int t = kTileCap + tid; t < tiles; t += kThreads) mx = max(mx, float_to_key(trow[t]));
     const uint32_t sorted = wave_sort_desc(mx);
     const int q = (K + 3) >> 2;
     const uint32_t wq = (uint32_t)__builtin_amdgcn_readlane((int)sorted, q - 1);
@@ -372,7 +367,8 @@ __global__ void __launch_bounds__(kThreads) topk_tiles_kernel(const float* __res
 
     // ---- the tiles that may hold a member of the top K
     for (int t = tid; t < tiles; t += kThreads) {
-        if (float_to_key(trow[t]) >= tau) {
+        const uint32_t k = staged ? tkey[t] : float_to_key(trow[t]);
+        if (k >= tau) {
             const int i = atomicAdd(&s_nsel, 1);
             if (i < kSelCap) sel[i] = t;
         }
@@ -381,14 +377,25 @@ __global__ void __launch_bounds__(kThreads) topk_tiles_kernel(const float* __res
     const int nsel = s_nsel;
     bool exact = nsel > kSelCap;
     if (!exact) {
-        // ---- their logits >= tau
-        for (int e = tid; e < nsel * 32; e += kThreads) {
-            const int v = sel[e >> 5] * 32 + (e & 31);
-            if (v < V) {
-                const uint32_t k = float_to_key(row[v]);
-                if (k >= tau) {
-                    const int i = atomicAdd(&s_ncand, 1);
-                    if (i < kCandCap) cand[i] = pack_entry(k, (uint32_t)v);
+        // ---- their logits >= tau (eight loads in flight per thread at a time)
+        for (int base = 0; base < nsel * 32; base += kThreads * 8) {
+            float zv[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int e = base + tid + kThreads * i;
+                const int v = e < nsel * 32 ? sel[e >> 5] * 32 + (e & 31) : V;
+                zv[i] = v < V ? row[v] : 0.f;
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int e = base + tid + kThreads * i;
+                const int v = e < nsel * 32 ? sel[e >> 5] * 32 + (e & 31) : V;
+                if (v < V) {
+                    const uint32_t k = float_to_key(zv[i]);
+                    if (k >= tau) {
+                        const int c = atomicAdd(&s_ncand, 1);
+                        if (c < kCandCap) cand[c] = pack_entry(k, (uint32_t)v);
+                    }
                 }
             }
         }
