@@ -361,6 +361,48 @@ def draft_block(hidden_bits, lm_head_bits, d2t, tables, gate_w, last_tok, K,
     return draft_from_logits(z, K, d2t, tables, hidden_bits, gate_w, last_tok, row_offsets, walk)
 
 
+# --------------------------------------------------------------------------
+# without a Markov head: the scaled, soft-capped rows and their argmax
+# --------------------------------------------------------------------------
+
+def scale_cap(z: np.ndarray, scale: float, cap: float) -> np.ndarray:
+    """The backbone rows as a draft without a Markov head uses them.
+
+    [G] commit "DFlash-2 Markov head / BlockRowSource": without a head the
+    selector scales and soft caps the backbone rows (the Markov head's rows
+    differ from them by the output multiplier and the soft cap).  The pages
+    give no formula; reading: the multiplier first, then the usual tanh cap,
+        z' = cap * tanh(scale * z / cap)   when cap > 0,
+        z' = scale * z                     otherwise (no cap),
+    with a positive multiplier.
+    """
+    assert scale > 0, "the output multiplier must be positive"
+    x = float(scale) * np.asarray(z, np.float64)
+    if cap > 0:
+        return float(cap) * np.tanh(x / float(cap))
+    return x
+
+
+def argmax_rows(z: np.ndarray, scale: float, cap: float, d2t: Optional[np.ndarray]):
+    """Greedy head-less drafting: per row the best token of the scaled, capped row.
+
+    [G] same commit: a greedy request whose logit processors keep the argmax
+    takes the best token of every row.  Ties go to the lowest draft id (the
+    index order of the TopP commit).  Returns (draft ids [M], target ids [M],
+    the winning z' [M]).
+    """
+    zs = scale_cap(z, scale, cap)
+    ids = np.array([_lowest_argmax(row) for row in zs], dtype=np.int64)
+    tok = draft_to_target(ids, d2t)
+    vals = zs[np.arange(zs.shape[0]), ids] if zs.shape[0] else np.zeros(0)
+    return ids, tok, vals
+
+
+def draft_argmax(hidden_bits, lm_head_bits, d2t, scale: float, cap: float):
+    """The whole head-less draft step: hidden states -> logits -> scaled, capped argmax."""
+    return argmax_rows(logits(hidden_bits, lm_head_bits), scale, cap, d2t)
+
+
 def check_d2t(d2t: np.ndarray, Vd: int, Vt: int):
     """(valid, injective): every i + d2t[i] lies in [0, V_t), and no two draft ids share a target.
 
