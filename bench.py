@@ -124,6 +124,11 @@ def main():
                   args.steps, 3)
     pair = api.pair_scores(ctok, tables, last_tok, gate_w=gate_w, hidden=hidden, block_len=L)
     k4_ms = timed(lambda: api.walk(ctok, un, pair, R, block_len=L, walk=args.walk), args.steps, 3)
+    # ---- the head-less draft step on the same rows (scaled, soft-capped argmax), timed alone
+    nh_tok = torch.empty(M, dtype=torch.int64, device="cuda")
+    nh_ms = timed(lambda: api.draft_argmax(hidden, W, d2t=d2t, target_vocab=Vt, out_scale=1.0, soft_cap=30.0,
+                                           workspace=ws, with_values=False, out=(nh_tok, None)), args.steps, 3)
+    log(f"head-less step (scale 1, soft cap 30, argmax): {nh_ms * 1e3:.1f} us")
     log(f"stages: lm_head {k1_ms * 1e3:.1f} us, top-k {k2_ms * 1e3:.1f} us, pair {k3_ms * 1e3:.1f} us, "
         f"walk {k4_ms * 1e3:.1f} us")
 
@@ -178,6 +183,8 @@ def main():
                      "mfma_frac": round(k1_tflops / BF16_MFMA_PEAK_TFLOPS, 4)},
         "standalone_topk_pass": {"achieved_gbs": round(k2_gbs, 1), "frac": round(k2_gbs / HBM_PEAK_GBS, 4),
                       "bytes_per_launch": k2_bytes, "avg_launch_us": round(k2_ms * 1e3, 2)},
+        "headless_step": {"us": round(nh_ms * 1e3, 2), "blocks_per_s": round(R / (nh_ms * 1e-3), 1),
+                          "out_scale": 1.0, "soft_cap": 30.0},
         "standalone_stages_us": {"lm_head": round(k1_ms * 1e3, 2), "topk": round(k2_ms * 1e3, 2),
                       "pair_scores": round(k3_ms * 1e3, 2), "walk": round(k4_ms * 1e3, 2)},
     }

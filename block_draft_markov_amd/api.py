@@ -118,6 +118,28 @@ def draft_block(hidden: torch.Tensor, lm_head_w: torch.Tensor, tables: torch.Ten
     return tokens, scores
 
 
+def draft_argmax(hidden: torch.Tensor, lm_head_w: torch.Tensor, *, d2t: Optional[torch.Tensor] = None,
+                 target_vocab: Optional[int] = None, out_scale: float = 1.0, soft_cap: float = 0.0,
+                 workspace: Optional[Workspace] = None, with_values: bool = True,
+                 out: Optional[Tuple[torch.Tensor, Optional[torch.Tensor]]] = None):
+    """Head-less draft step: (tokens int64 [M], winning scaled/capped logits fp32 [M] or None)."""
+    _bf16(hidden, "hidden"), _bf16(lm_head_w, "lm_head"), _expect(d2t, torch.int64, "d2t")
+    M, H = hidden.shape
+    Vd = lm_head_w.shape[0]
+    Vt = target_vocab if target_vocab is not None else Vd
+    d = make_dims(R=M, L=1, M=M, H=H, Vd=Vd, Vt=Vt, K=min(64, Vd))
+    dev = hidden.device
+    if out is None:
+        tokens = torch.empty(M, dtype=torch.int64, device=dev)
+        values = torch.empty(M, dtype=torch.float32, device=dev) if with_values else None
+    else:
+        tokens, values = out
+    wsp, wsn = _ws(workspace, dev).get(workspace_bytes(d))
+    check(load().dflash_draft_argmax(ctypes.byref(d), _ptr(hidden), _ptr(lm_head_w), _ptr(d2t), float(out_scale),
+                                     float(soft_cap), _ptr(tokens), _ptr(values), wsp, wsn, _stream(dev)))
+    return tokens, values
+
+
 def lm_head(hidden: torch.Tensor, lm_head_w: torch.Tensor, *, workspace: Optional[Workspace] = None,
             with_lse: bool = True, out: Optional[torch.Tensor] = None):
     """Part 1: (logits fp32 [M, V_d] (a view of rows of stride dflash_logits_stride), lse fp32 [M] or None)."""

@@ -5,6 +5,8 @@
 #include "../../include/dflash_draft.h"
 #include "internal.hpp"
 
+#include <cmath>
+
 #include <hip/hip_runtime.h>
 
 #include <stdarg.h>
@@ -194,6 +196,37 @@ int dflash_draft_block(const dflash_dims* d, const uint16_t* hidden, const uint1
                                  row_offsets, d->num_requests, d->block_len, d->total_rows, d->top_k, d->walk,
                                  tokens, scores, nullptr, s)) != hipSuccess)
         return hip_fail(e, "walk launch");
+    return ok();
+}
+
+int dflash_draft_argmax(const dflash_dims* d, const uint16_t* hidden, const uint16_t* lm_head, const int64_t* d2t,
+                        float out_scale, float soft_cap, int64_t* tokens, float* values, void* ws, size_t ws_bytes,
+                        void* stream) {
+    int rc;
+    if ((rc = check_dims(d))) return rc;
+    const int64_t M = d->total_rows;
+    if ((rc = need(hidden, M, "hidden")) || (rc = need(lm_head, 1, "lm_head")) || (rc = need(tokens, M, "tokens")))
+        return rc;
+    if (!(out_scale > 0.f) || !std::isfinite(out_scale))
+        return fail(DFLASH_EINVAL, "out_scale = %g must be finite and positive", (double)out_scale);
+    if (!std::isfinite(soft_cap)) return fail(DFLASH_EINVAL, "soft_cap = %g must be finite", (double)soft_cap);
+    if (d->target_vocab > d->draft_vocab && !d2t)
+        return fail(DFLASH_EINVAL, "target_vocab = %d > draft_vocab = %d needs d2t", d->target_vocab,
+                    d->draft_vocab);
+    if (!aligned(hidden, 16) || !aligned(lm_head, 16))
+        return fail(DFLASH_EINVAL, "hidden and lm_head must be 16-byte aligned");
+    Layout l;
+    if ((rc = check_ws(d, ws, ws_bytes, l))) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    float* logits = at<float>(ws, l.logits);
+    float* tmax = l.ldt ? at<float>(ws, l.tmax) : nullptr;
+    if ((e = dflash::launch_lmhead(hidden, lm_head, logits, l.ldz, at<float2>(ws, l.part), tmax, l.ldt,
+                                   d->total_rows, d->hidden, d->draft_vocab, s)) != hipSuccess)
+        return hip_fail(e, "lm_head launch");
+    if ((e = dflash::launch_argmax(logits, l.ldz, tmax, l.ldt, d2t, d->total_rows, d->draft_vocab, out_scale,
+                                   soft_cap, tokens, values, s)) != hipSuccess)
+        return hip_fail(e, "argmax launch");
     return ok();
 }
 

@@ -37,6 +37,12 @@ hipError_t launch_topk_tiles(const float* logits, int64_t ldz, const float* tile
                              const float2* lse_part, int nparts, const int64_t* d2t, int M, int V, int K,
                              int32_t* cand_idx, int64_t* cand_tok, float* unary, hipStream_t s);
 
+// Head-less drafting: per row the lowest draft id maximizing the scaled, soft-capped
+// logit, from the tile maxima when given (ldt > 0), else from a scan of the row.
+hipError_t launch_argmax(const float* logits, int64_t ldz, const float* tile_max, int64_t ldt,
+                         const int64_t* d2t, int M, int V, float scale, float cap, int64_t* tokens,
+                         float* values, hipStream_t s);
+
 // ---------------------------------------------------------------- parts 3 and 4: lattice
 hipError_t launch_pair_scores(const int64_t* cand_tok, const float* tables, const float* gate_w,
                               const uint16_t* hidden, const int64_t* last_tok,

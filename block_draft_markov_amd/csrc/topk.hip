@@ -468,6 +468,136 @@ hipError_t launch_topk(const float* logits, int64_t ldz, const float* lse, const
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- head-less argmax
+// f(z) = cap tanh(scale z / cap) (cap > 0) or scale z is non-decreasing, so every
+// logit with f(z) = max f lies in a tile whose maximum m_t has f(m_t) = max f:
+// with tile maxima only those tiles are read.  Ties go to the lowest id.
+__device__ __forceinline__ float scale_cap(float x, float scale, float cap) {
+    return cap > 0.f ? cap * tanhf(scale * x / cap) : scale * x;
+}
+
+// (value, id) with the larger value, the lower id on a tie.
+__device__ __forceinline__ void better(float& v, int& i, float v2, int i2) {
+    if (v2 > v || (v2 == v && i2 < i)) { v = v2; i = i2; }
+}
+
+__global__ void __launch_bounds__(kThreads) argmax_kernel(const float* __restrict__ logits, int64_t ldz,
+                                                          const float* __restrict__ tmax, int64_t ldt, int V,
+                                                          float scale, float cap, const int64_t* __restrict__ d2t,
+                                                          int64_t* __restrict__ tokens, float* __restrict__ values) {
+    __shared__ float tf[kTileCap];     // z' of the tile maxima (rows of at most kTileCap tiles)
+    __shared__ int sel[kSelCap];
+    __shared__ float s_v[4];
+    __shared__ int s_i[4];
+    __shared__ int s_best, s_nsel;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int m = blockIdx.x;
+    const float* row = logits + (int64_t)m * ldz;
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+    // block-wide (max, lowest id)
+    auto reduce = [&]() {
+        for (int o = 32; o > 0; o >>= 1) {
+            const float v2 = __shfl_xor(bv, o);
+            const int i2 = __shfl_xor(bi, o);
+            better(bv, bi, v2, i2);
+        }
+        __syncthreads();
+        if (lane == 0) { s_v[w] = bv; s_i[w] = bi; }
+        __syncthreads();
+        bv = s_v[0]; bi = s_i[0];
+        for (int q = 1; q < 4; ++q) better(bv, bi, s_v[q], s_i[q]);
+    };
+    // every logit of the row, sixteen loads in flight per thread at a time
+    auto scan_row = [&]() {
+        bv = -INFINITY;
+        bi = 0x7fffffff;
+        for (int base = 0; base < V; base += kThreads * 16) {
+            float zv[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int v = base + tid + kThreads * i;
+                zv[i] = v < V ? row[v] : -INFINITY;
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int v = base + tid + kThreads * i;
+                if (v < V) better(bv, bi, scale_cap(zv[i], scale, cap), v);
+            }
+        }
+        reduce();
+    };
+    const int tiles = (V + 31) / 32;
+    if (tmax && tiles <= kTileCap) {
+        const float* trow = tmax + (int64_t)m * ldt;
+        constexpr int kTPT = kTileCap / kThreads;
+        float tv[kTPT];
+#pragma unroll
+        for (int i = 0; i < kTPT; ++i) {
+            const int t = tid + kThreads * i;
+            tv[i] = t < tiles ? trow[t] : -INFINITY;
+        }
+#pragma unroll
+        for (int i = 0; i < kTPT; ++i) {
+            const int t = tid + kThreads * i;
+            if (t < tiles) {
+                const float f = scale_cap(tv[i], scale, cap);
+                tf[t] = f;
+                better(bv, bi, f, t);
+            }
+        }
+        if (tid == 0) { s_best = 0x7fffffff; s_nsel = 0; }
+        reduce();
+        const float fmax = bv;
+        // the tiles that reach fmax
+        for (int t = tid; t < tiles; t += kThreads) {
+            if (tf[t] == fmax) {
+                const int i = atomicAdd(&s_nsel, 1);
+                if (i < kSelCap) sel[i] = t;
+            }
+        }
+        __syncthreads();
+        const int nsel = s_nsel;
+        if (nsel <= kSelCap) {
+            for (int base = 0; base < nsel * 32; base += kThreads * 8) {
+                float zv[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int e = base + tid + kThreads * i;
+                    const int v = e < nsel * 32 ? sel[e >> 5] * 32 + (e & 31) : V;
+                    zv[i] = v < V ? row[v] : -INFINITY;
+                }
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int e = base + tid + kThreads * i;
+                    const int v = e < nsel * 32 ? sel[e >> 5] * 32 + (e & 31) : V;
+                    if (v < V && scale_cap(zv[i], scale, cap) == fmax) atomicMin(&s_best, v);
+                }
+            }
+            __syncthreads();
+            bi = s_best;
+            bv = fmax;
+        } else {
+            scan_row();   // heavy ties: every logit
+        }
+    } else {
+        scan_row();
+    }
+    if (bi == 0x7fffffff) bi = 0;   // NaN rows match nothing: id 0
+    if (tid == 0) {
+        tokens[m] = d2t ? (int64_t)bi + d2t[bi] : (int64_t)bi;
+        if (values) values[m] = bv;
+    }
+}
+
+hipError_t launch_argmax(const float* logits, int64_t ldz, const float* tile_max, int64_t ldt, const int64_t* d2t,
+                         int M, int V, float scale, float cap, int64_t* tokens, float* values, hipStream_t s) {
+    if (M <= 0) return hipSuccess;
+    hipLaunchKernelGGL(argmax_kernel, dim3(M), dim3(kThreads), 0, s, logits, ldz, ldt > 0 ? tile_max : nullptr, ldt,
+                       V, scale, cap, d2t, tokens, values);
+    return hipGetLastError();
+}
+
 int topk_tiles_chunks(int V) { return (V + kThreads * 64 - 1) / (kThreads * 64); }
 
 hipError_t launch_topk_tiles(const float* logits, int64_t ldz, const float* tile_max, int64_t ldt,

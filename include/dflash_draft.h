@@ -159,6 +159,25 @@ int dflash_walk(const dflash_dims* dims, const int64_t* cand_tok, const float* u
                 const float* pair, const int32_t* row_offsets,
                 int64_t* tokens, float* scores, int32_t* slots, void* stream);
 
+/* Head-less draft step (openvino.genai page, commit "DFlash-2 Markov head /
+ * BlockRowSource": without a Markov head the selector scales and soft caps
+ * the backbone rows, and a greedy request takes the best token of every row).
+ * For every row m of hidden bf16 [M][H]:
+ *   z'_m[v] = soft_cap * tanh(out_scale * z_m[v] / soft_cap)   when soft_cap > 0,
+ *           = out_scale * z_m[v]                               otherwise,
+ *   with z_m = W h_m as in dflash_draft_block;
+ *   tokens out int64 [M] = t(i_m), i_m = the lowest draft id maximizing z'_m,
+ *   t(i) = i + d2t[i] (i when d2t is NULL);
+ *   values out fp32 [M] = z'_m[i_m], or NULL to skip.
+ * dims: total_rows, hidden, draft_vocab and target_vocab as for
+ * dflash_draft_block (the other fields must be valid and are not used).
+ * out_scale must be finite and > 0 (DFLASH_EINVAL otherwise); soft_cap must
+ * be finite.  Workspace: dflash_workspace_bytes(dims) bytes, 256-byte aligned.
+ * The maximum is taken in fp32 on the kernel's z' values. */
+int dflash_draft_argmax(const dflash_dims* dims, const uint16_t* hidden, const uint16_t* lm_head,
+                        const int64_t* d2t, float out_scale, float soft_cap, int64_t* tokens,
+                        float* values, void* workspace, size_t workspace_bytes, void* stream);
+
 /* HOST memory: checks once, at set-up, that every i + d2t[i] lies in
  * [0, V_t) (returns DFLASH_EINVAL naming the first bad i otherwise) and
  * writes 1 to *is_injective when no two draft ids share a target id, else 0
