@@ -403,6 +403,70 @@ def draft_argmax(hidden_bits, lm_head_bits, d2t, scale: float, cap: float):
     return argmax_rows(logits(hidden_bits, lm_head_bits), scale, cap, d2t)
 
 
+# --------------------------------------------------------------------------
+# the dense Markov walk: one biased argmax per position
+# --------------------------------------------------------------------------
+
+@dataclass
+class DenseResult:
+    ids: np.ndarray       # int64 [M] chosen draft ids
+    tokens: np.ndarray    # int64 [M] chosen target ids
+    values: np.ndarray    # float64 [M] the winning biased value
+    margins: np.ndarray   # float64 [M] gap between the best and the second best value of the row
+
+
+def dense_row(z_row: np.ndarray, scale: float, cap: float, d2t, tables: np.ndarray, prev_tok: int):
+    """The biased row of one position and its lowest-id argmax.
+
+    [G] commit "DFlash-2 Markov head / BlockRowSource": a dense Markov step is
+    run per position and biases the scaled rows by the token drafted before;
+    a greedy request takes the best biased token.  [G] Description: the dense
+    walk (markov_head_top_k = 0, DSpark only: no gate) corrects every drafted
+    position.  Reading: the bias of draft id v after token s is the pairwise
+    term of the Top-K lattice, <A[s], B[t(v)]> with t(v) = v + d2t[v], added to
+    the scaled, soft-capped row.
+    """
+    Vd = z_row.shape[0]
+    t_all = draft_to_target(np.arange(Vd), d2t)
+    A = np.asarray(tables[0], np.float64)[int(prev_tok)]
+    B = np.asarray(tables[1], np.float64)[t_all]           # [V_d, r]
+    row = scale_cap(z_row, scale, cap) + B @ A
+    c = _lowest_argmax(row)
+    second = np.max(np.delete(row, c)) if Vd > 1 else -np.inf
+    return c, row[c], row[c] - second
+
+
+def dense_walk(z: np.ndarray, scale: float, cap: float, d2t, tables, last_tok, row_offsets=None,
+               prev_override: Optional[np.ndarray] = None) -> DenseResult:
+    """The dense walk of every request: s_0 = last accepted token, s_{p+1} = t(c_p).
+
+    prev_override [M] (optional) gives the previous token of every row instead
+    of the walk's own choice (to re-check another walk's decisions one by one).
+    """
+    R = len(last_tok)
+    M = z.shape[0]
+    off = _offsets(R, M, row_offsets)
+    ids = np.zeros(M, np.int64)
+    vals = np.zeros(M)
+    margins = np.full(M, np.inf)
+    for r in range(R):
+        a, b = int(off[r]), int(off[r + 1])
+        s = int(last_tok[r])
+        for m in range(a, b):
+            if prev_override is not None:
+                s = int(prev_override[m])
+            c, v, g = dense_row(z[m], scale, cap, d2t, tables, s)
+            ids[m], vals[m], margins[m] = c, v, g
+            s = int(draft_to_target(np.array([c]), d2t)[0])
+    return DenseResult(ids, draft_to_target(ids, d2t), vals, margins)
+
+
+def draft_dense(hidden_bits, lm_head_bits, d2t, tables, last_tok, scale: float, cap: float,
+                row_offsets=None) -> DenseResult:
+    """The whole dense-walk draft step."""
+    return dense_walk(logits(hidden_bits, lm_head_bits), scale, cap, d2t, tables, last_tok, row_offsets)
+
+
 def check_d2t(d2t: np.ndarray, Vd: int, Vt: int):
     """(valid, injective): every i + d2t[i] lies in [0, V_t), and no two draft ids share a target.
 
