@@ -129,6 +129,11 @@ def main():
     nh_ms = timed(lambda: api.draft_argmax(hidden, W, d2t=d2t, target_vocab=Vt, out_scale=1.0, soft_cap=30.0,
                                            workspace=ws, with_values=False, out=(nh_tok, None)), args.steps, 3)
     log(f"head-less step (scale 1, soft cap 30, argmax): {nh_ms * 1e3:.1f} us")
+    # ---- the dense Markov walk on the same rows and tables (no gate), timed alone
+    dn_ms = timed(lambda: api.draft_dense(hidden, W, tables, last_tok, d2t=d2t, block_len=L, out_scale=1.0,
+                                          soft_cap=30.0, workspace=ws, with_values=False, out=(nh_tok, None)),
+                  args.steps, 3)
+    log(f"dense walk step (scale 1, soft cap 30): {dn_ms * 1e3:.1f} us")
     log(f"stages: lm_head {k1_ms * 1e3:.1f} us, top-k {k2_ms * 1e3:.1f} us, pair {k3_ms * 1e3:.1f} us, "
         f"walk {k4_ms * 1e3:.1f} us")
 
@@ -185,6 +190,10 @@ def main():
                       "bytes_per_launch": k2_bytes, "avg_launch_us": round(k2_ms * 1e3, 2)},
         "headless_step": {"us": round(nh_ms * 1e3, 2), "blocks_per_s": round(R / (nh_ms * 1e-3), 1),
                           "out_scale": 1.0, "soft_cap": 30.0},
+        "dense_step": {"us": round(dn_ms * 1e3, 2), "blocks_per_s": round(R / (dn_ms * 1e-3), 1),
+                       "out_scale": 1.0, "soft_cap": 30.0,
+                       # per position: the gathered B rows of every draft id and the rows' logits
+                       "bytes_per_position": Vd * r * 4 + R * Vd * 4},
         "standalone_stages_us": {"lm_head": round(k1_ms * 1e3, 2), "topk": round(k2_ms * 1e3, 2),
                       "pair_scores": round(k3_ms * 1e3, 2), "walk": round(k4_ms * 1e3, 2)},
     }

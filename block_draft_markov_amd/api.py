@@ -140,6 +140,34 @@ def draft_argmax(hidden: torch.Tensor, lm_head_w: torch.Tensor, *, d2t: Optional
     return tokens, values
 
 
+def draft_dense(hidden: torch.Tensor, lm_head_w: torch.Tensor, tables: torch.Tensor, last_tok: torch.Tensor, *,
+                d2t: Optional[torch.Tensor] = None, row_offsets: Optional[torch.Tensor] = None,
+                block_len: Optional[int] = None, out_scale: float = 1.0, soft_cap: float = 0.0,
+                workspace: Optional[Workspace] = None, with_values: bool = True,
+                out: Optional[Tuple[torch.Tensor, Optional[torch.Tensor]]] = None):
+    """Dense Markov walk: (tokens int64 [M], winning biased values fp32 [M] or None)."""
+    _bf16(hidden, "hidden"), _bf16(lm_head_w, "lm_head")
+    _expect(tables, torch.float32, "tables"), _expect(last_tok, torch.int64, "last_tok")
+    _expect(d2t, torch.int64, "d2t"), _expect(row_offsets, torch.int32, "row_offsets")
+    M, H = hidden.shape
+    Vd = lm_head_w.shape[0]
+    Vt, r = tables.shape[1], tables.shape[2]
+    R = last_tok.shape[0]
+    L = block_len if block_len is not None else (M // R if R else 1)
+    d = make_dims(R=R, L=L, M=M, H=H, Vd=Vd, Vt=Vt, K=min(64, Vd), r=r)
+    dev = hidden.device
+    if out is None:
+        tokens = torch.empty(M, dtype=torch.int64, device=dev)
+        values = torch.empty(M, dtype=torch.float32, device=dev) if with_values else None
+    else:
+        tokens, values = out
+    wsp, wsn = _ws(workspace, dev).get(workspace_bytes(d))
+    check(load().dflash_draft_dense(ctypes.byref(d), _ptr(hidden), _ptr(lm_head_w), _ptr(d2t), _ptr(tables),
+                                    _ptr(last_tok), _ptr(row_offsets), float(out_scale), float(soft_cap),
+                                    _ptr(tokens), _ptr(values), wsp, wsn, _stream(dev)))
+    return tokens, values
+
+
 def lm_head(hidden: torch.Tensor, lm_head_w: torch.Tensor, *, workspace: Optional[Workspace] = None,
             with_lse: bool = True, out: Optional[torch.Tensor] = None):
     """Part 1: (logits fp32 [M, V_d] (a view of rows of stride dflash_logits_stride), lse fp32 [M] or None)."""

@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdflash_draft.so")
-SOURCES = ["abi.hip", "lmhead.hip", "topk.hip", "lattice.hip"]
+SOURCES = ["abi.hip", "lmhead.hip", "topk.hip", "lattice.hip", "dense.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops off: packed fp32 VALU forms are never emitted.

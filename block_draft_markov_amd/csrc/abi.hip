@@ -93,7 +93,7 @@ int need(const void* p, int64_t count, const char* name) {
 struct Layout {
     int64_t ldz;
     int64_t ldt;      // tile maxima stride (0: none, the Top-K reads every logit)
-    size_t logits, lse, part, tmax, best, cidx, ctok, unary, pair, total;
+    size_t logits, lse, part, tmax, best, cidx, ctok, unary, pair, dense, total;
     int nparts;
 };
 
@@ -119,6 +119,7 @@ Layout layout(const dflash_dims* d) {
     l.ctok = take((size_t)(M * K) * sizeof(int64_t));
     l.unary = take((size_t)(M * K) * sizeof(float));
     l.pair = take((size_t)(M * K * K) * sizeof(float));
+    l.dense = take((size_t)((int64_t)d->num_requests * d->block_len) * sizeof(uint64_t));
     l.total = off > 0 ? off : 256;
     return l;
 }
@@ -227,6 +228,39 @@ int dflash_draft_argmax(const dflash_dims* d, const uint16_t* hidden, const uint
     if ((e = dflash::launch_argmax(logits, l.ldz, tmax, l.ldt, d2t, d->total_rows, d->draft_vocab, out_scale,
                                    soft_cap, tokens, values, s)) != hipSuccess)
         return hip_fail(e, "argmax launch");
+    return ok();
+}
+
+int dflash_draft_dense(const dflash_dims* d, const uint16_t* hidden, const uint16_t* lm_head, const int64_t* d2t,
+                       const float* tables, const int64_t* last_tok, const int32_t* row_offsets, float out_scale,
+                       float soft_cap, int64_t* tokens, float* values, void* ws, size_t ws_bytes, void* stream) {
+    int rc;
+    if ((rc = check_dims(d)) || (rc = check_rows(d, row_offsets))) return rc;
+    const int64_t M = d->total_rows, R = d->num_requests;
+    if ((rc = need(hidden, M, "hidden")) || (rc = need(lm_head, 1, "lm_head")) || (rc = need(tables, 1, "tables")) ||
+        (rc = need(last_tok, R, "last_tok")) || (rc = need(tokens, M, "tokens")))
+        return rc;
+    if (!(out_scale > 0.f) || !std::isfinite(out_scale))
+        return fail(DFLASH_EINVAL, "out_scale = %g must be finite and positive", (double)out_scale);
+    if (!std::isfinite(soft_cap)) return fail(DFLASH_EINVAL, "soft_cap = %g must be finite", (double)soft_cap);
+    if (d->target_vocab > d->draft_vocab && !d2t)
+        return fail(DFLASH_EINVAL, "target_vocab = %d > draft_vocab = %d needs d2t", d->target_vocab,
+                    d->draft_vocab);
+    if (!aligned(hidden, 16) || !aligned(lm_head, 16))
+        return fail(DFLASH_EINVAL, "hidden and lm_head must be 16-byte aligned");
+    Layout l;
+    if ((rc = check_ws(d, ws, ws_bytes, l))) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    float* logits = at<float>(ws, l.logits);
+    if ((e = dflash::launch_lmhead(hidden, lm_head, logits, l.ldz, at<float2>(ws, l.part), nullptr, 0,
+                                   d->total_rows, d->hidden, d->draft_vocab, s)) != hipSuccess)
+        return hip_fail(e, "lm_head launch");
+    if ((e = dflash::launch_dense_walk(logits, l.ldz, d2t, tables, last_tok, row_offsets, d->num_requests,
+                                       d->block_len, d->total_rows, d->draft_vocab, d->target_vocab, d->rank,
+                                       out_scale, soft_cap, at<uint64_t>(ws, l.dense), tokens, values, s)) !=
+        hipSuccess)
+        return hip_fail(e, "dense walk launch");
     return ok();
 }
 

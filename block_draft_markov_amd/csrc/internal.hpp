@@ -48,6 +48,12 @@ hipError_t launch_pair_scores(const int64_t* cand_tok, const float* tables, cons
                               const uint16_t* hidden, const int64_t* last_tok,
                               const int32_t* row_offsets, int R, int L, int M, int H, int Vt,
                               int K, int r, float* pair, hipStream_t s);
+// The dense Markov walk: per position every request's scaled, soft-capped row biased by
+// <A[previous token], B[t(v)]> and its lowest-id argmax; best [L][R] packed entries.
+hipError_t launch_dense_walk(const float* logits, int64_t ldz, const int64_t* d2t, const float* tables,
+                             const int64_t* last_tok, const int32_t* row_offsets, int R, int L, int M, int V,
+                             int Vt, int r, float scale, float cap, uint64_t* best, int64_t* tokens, float* values,
+                             hipStream_t s);
 hipError_t launch_walk(const int64_t* cand_tok, const float* unary, const float* pair,
                        const int32_t* row_offsets, int R, int L, int M, int K, int walk,
                        int64_t* tokens, float* scores, int32_t* slots, hipStream_t s);

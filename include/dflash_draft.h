@@ -178,6 +178,29 @@ int dflash_draft_argmax(const dflash_dims* dims, const uint16_t* hidden, const u
                         const int64_t* d2t, float out_scale, float soft_cap, int64_t* tokens,
                         float* values, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Dense Markov walk (openvino.genai page "Add DSpark and DFlash v2 drafts ...",
+ * Description: with markov_head_top_k = 0 the head, DSpark only, corrects
+ * every drafted position, one inference per position; commit "DFlash-2 Markov
+ * head / BlockRowSource": the dense step biases the scaled rows by the token
+ * drafted before and a greedy request takes the best biased token).  For
+ * request r with rows m(0) .. m(n-1), s_0 = last_tok[r]:
+ *   x_p[v] = z'_{m(p)}[v] + <A[s_p], B[t(v)]>   over all draft ids v,
+ *   c_p    = the lowest draft id maximizing x_p,   s_{p+1} = t(c_p),
+ * z' the scaled, soft-capped rows of dflash_draft_argmax, t and the tables
+ * fp32 [2][V_t][r] as in dflash_draft_block (no gate).
+ *   tokens out int64 [M] = t(c_p); values out fp32 [M] = x_p[c_p], or NULL.
+ * dims as for dflash_draft_block (top_k and walk must be valid and are not
+ * used); row_offsets int32 [R+1] or NULL; out_scale finite and > 0,
+ * soft_cap finite (DFLASH_EINVAL otherwise).  Workspace:
+ * dflash_workspace_bytes(dims) bytes, 256-byte aligned.  Products and sums in
+ * fp32; the maximum is taken in fp32 on the kernel's x values.  One launch per
+ * position follows the lm_head launch on `stream`. */
+int dflash_draft_dense(const dflash_dims* dims, const uint16_t* hidden, const uint16_t* lm_head,
+                       const int64_t* d2t, const float* tables, const int64_t* last_tok,
+                       const int32_t* row_offsets, float out_scale, float soft_cap,
+                       int64_t* tokens, float* values, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
 /* HOST memory: checks once, at set-up, that every i + d2t[i] lies in
  * [0, V_t) (returns DFLASH_EINVAL naming the first bad i otherwise) and
  * writes 1 to *is_injective when no two draft ids share a target id, else 0

@@ -44,7 +44,7 @@ def err(lib):
 
 def test_every_declared_symbol_is_exported(lib):
     names = header_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     for n in names:
         assert hasattr(lib, n), f"{n} declared in include/ but not exported"
     assert set(names) == set(bdm.SIGNATURES), "binding and header disagree"
@@ -239,3 +239,25 @@ def test_draft_argmax_validates(lib):
     assert call(hidden=FAKE + 2) == bdm.EINVAL and "aligned" in err(lib)
     assert call(wsn=16) == bdm.EWORKSPACE
     assert call(d=dims(top_k=0)) == bdm.EINVAL and "top_k" in err(lib)
+
+
+def test_draft_dense_validates(lib):
+    d = dims()
+    big = 1 << 40
+    call = lambda **p: lib.dflash_draft_dense(
+        ctypes.byref(p.get("d", d)), p.get("hidden", FAKE), p.get("lm", FAKE), p.get("d2t", None),
+        p.get("tables", FAKE), p.get("last", FAKE), p.get("offs", None), p.get("scale", 1.0), p.get("cap", 0.0),
+        p.get("tok", FAKE), p.get("val", None), p.get("ws", FAKE), p.get("wsn", big), None)
+    assert call(scale=0.0) == bdm.EINVAL and "out_scale" in err(lib)
+    assert call(scale=float("nan")) == bdm.EINVAL and "out_scale" in err(lib)
+    assert call(cap=float("inf")) == bdm.EINVAL and "soft_cap" in err(lib)
+    assert call(tables=None) == bdm.EINVAL and "tables" in err(lib)
+    assert call(last=None) == bdm.EINVAL and "last_tok" in err(lib)
+    assert call(tok=None) == bdm.EINVAL and "tokens" in err(lib)
+    assert call(hidden=None) == bdm.EINVAL and "hidden" in err(lib)
+    assert call(d=dims(target_vocab=2000)) == bdm.EINVAL and "d2t" in err(lib)
+    assert call(lm=FAKE_ODD) == bdm.EINVAL and "aligned" in err(lib)
+    assert call(d=dims(total_rows=5)) == bdm.EINVAL and "row_offsets" in err(lib)
+    assert call(ws=None) == bdm.EWORKSPACE
+    assert call(wsn=16) == bdm.EWORKSPACE
+    assert call(d=dims(rank=0)) == bdm.EINVAL and "rank" in err(lib)
