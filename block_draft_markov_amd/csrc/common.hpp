@@ -38,6 +38,27 @@ __device__ __forceinline__ uint32_t entry_key(uint64_t e) { return (uint32_t)(e 
 __device__ __forceinline__ uint32_t entry_id(uint64_t e) { return 0xFFFFFFFFu - (uint32_t)e; }
 constexpr uint64_t kEmptyEntry = 0;  // key 0, id 0xFFFFFFFF: below every real entry
 
+// ---------------------------------------------------------------- head transform
+// The scaled, soft-capped logit of the head-less rows in fp32: scale * z, or
+// cap * tanh(scale * z / cap) when cap > 0, with tanh |y| = (1 - e) / (1 + e),
+// e = 2^(-2 log2(e) |y|), from the hardware exp2 and reciprocal: about 10
+// instructions and no division.  The absolute error of tanh is a few 1e-8; every
+// step is non-decreasing in |y| (1 - e and 1 / (1 + e) fall with e, and rounding keeps
+// order), so the transform is non-decreasing in z, which the tile-maxima argmax uses.
+struct HeadMap {
+    float scale, a, cap;   // a = scale / cap, computed once
+    bool capped;
+};
+__device__ __forceinline__ HeadMap head_map(float scale, float cap) {
+    return {scale, cap > 0.f ? scale / cap : 0.f, cap, cap > 0.f};
+}
+__device__ __forceinline__ float head_apply(const HeadMap& h, float z) {
+    const float y = h.a * z;
+    const float e = __builtin_amdgcn_exp2f(-2.8853900817779268f * fabsf(y));
+    const float t = (1.f - e) * __builtin_amdgcn_rcpf(1.f + e);
+    return h.capped ? h.cap * copysignf(t, y) : h.scale * z;
+}
+
 // ---------------------------------------------------------------- wave reductions (DPP)
 // DPP controls of the gfx9 family: quad permutes and row rotates within rows
 // of 16 lanes; readlane combines the four rows.

@@ -8,12 +8,14 @@
 //   x_p[v] = f(z_m[v]) + <A[s_p], B[t(v)]>,   c_p = the lowest v maximizing x_p,
 // f the scale and soft cap of the head-less rows, t(v) = v + d2t[v].
 //
-// One launch per position (the next position needs every request's choice).
-// A workgroup takes 256 vocabulary ids for up to kGroup requests; the biases
-// are a small fp32 GEMM (requests x ids x rank) on the matrix cores; (x, id)
-// per request reduces to one packed 64-bit entry (order-preserving key of x << 32 | ~id, so the maximum
-// entry is the largest x with the lowest id); one atomicMax per request and
-// workgroup merges the workgroups.
+// One launch per position (the next position needs every request's choice).  A
+// workgroup takes kIds vocabulary ids (kTpw tiles of 32 per wave) for up to kGroup
+// requests; the biases are a small fp32 GEMM (ids x requests x rank) on the matrix
+// cores, fed by B rows streamed through registers a 128-byte line at a time and the
+// requests' A rows staged in LDS.  Per request the largest x with the lowest id is
+// packed into one 64-bit entry (order-preserving key of x << 32 | ~id); one atomicMax
+// per request and workgroup merges the workgroups.  The kernel is bound by the B
+// stream: V_d r 4 bytes per position, every position.
 
 #include "common.hpp"
 #include "internal.hpp"
@@ -26,12 +28,19 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kGroup = 32;     // requests per workgroup
+constexpr int kBufWord3 = 0x00020000;   // gfx9 buffer descriptor word 3: raw dword access
+constexpr int kBig = 0x40000000;        // buffer offset past the end of every table the buffer path takes
 constexpr int kRankChunk = 256; // rank elements of the A rows staged in LDS at a time
+#ifndef DENSE_AHEAD
+#define DENSE_AHEAD 1
+#endif
+#ifndef DENSE_TPW
+#define DENSE_TPW 3
+#endif
+constexpr int kAhead = DENSE_AHEAD;   // 32-element slots of B in flight ahead of the MFMAs
+constexpr int kTpw = DENSE_TPW;       // 32-id vocab tiles per wave
+constexpr int kIds = 4 * 32 * kTpw;   // vocab ids per workgroup
 constexpr int kAStride = kRankChunk + 4;   // padded row stride: the 32 rows of a read hit distinct banks
-
-__device__ __forceinline__ float head_scale_cap(float x, float scale, float cap) {
-    return cap > 0.f ? cap * tanhf(scale * x / cap) : scale * x;
-}
 
 __device__ __forceinline__ void rows_of(const int32_t* row_offsets, int req, int L, int M, int& a, int& n) {
     if (row_offsets) {
@@ -53,12 +62,16 @@ __global__ void __launch_bounds__(kThreads) dense_clear_kernel(uint64_t* best, i
     if (i < n) best[i] = 0;
 }
 
-// One position for kGroup (32) requests and 256 vocabulary ids: wave w computes the
-// 32 x 32 bias tiles of vocab tiles 2w and 2w + 1 with v_mfma_f32_32x32x2_f32
-// (fp32 products and sums).  Operands: in MFMA step s lane l supplies A[l % 32][k]
-// and B[k][l % 32] with k = 8 (s / 4) + 4 (l / 32) + s % 4, the same index in both,
-// so every lane reads 4 consecutive rank elements per 4 steps.  Result register i
-// of lane l is request 8 (i / 4) + 4 (l / 32) + i % 4 at vocab id l % 32 of the tile.
+// One position for kGroup (32) requests and kIds vocabulary ids: wave w computes the
+// bias of kTpw tiles of 32 ids for the 32 requests with v_mfma_f32_32x32x2_f32 (fp32
+// products and sums), the B rows of the ids as the row operand and the A rows of the
+// requests' previous tokens (staged in LDS) as the column operand.  In MFMA step s lane l
+// supplies B[t(id l % 32)][k] and A[s(request l % 32)][k] with k = 8 (s / 4) + 4 (l / 32)
+// + s % 4, the same index in both, so a lane reads 4 consecutive rank elements per 4
+// steps.  Result register i of lane l is id 8 (i / 4) + 4 (l / 32) + i % 4 of the tile
+// for request l % 32: a lane holds 16 ids of one request, so the argmax is taken in
+// the lane and finished with one exchange between the two halves of the wave.
+template <bool kVec>
 __global__ void __launch_bounds__(kThreads) dense_pos_kernel(
     const float* __restrict__ logits, int64_t ldz, const int64_t* __restrict__ d2t,
     const float* __restrict__ tables, const int64_t* __restrict__ last_tok, const int32_t* __restrict__ row_offsets,
@@ -74,6 +87,62 @@ __global__ void __launch_bounds__(kThreads) dense_pos_kernel(
     const int ng = min(kGroup, R - g0);
     const float* TA = tables;
     const float* TB = tables + (int64_t)Vt * r;
+
+    // the B rows of this lane's vocab ids in the wave's tiles
+    const int vt0 = blockIdx.x * kIds + w * 32 * kTpw;   // first id of the wave's tiles
+    const float* brow[kTpw];
+    bool bok[kTpw];
+#pragma unroll
+    for (int j = 0; j < kTpw; ++j) {
+        const int v = vt0 + 32 * j + lr;
+        bok[j] = v < V;
+        int64_t t = bok[j] ? target_of(v, d2t) : 0;
+        t = t < 0 ? 0 : (t >= Vt ? (int64_t)Vt - 1 : t);
+        brow[j] = TB + t * r;
+    }
+    // Loads without branches or selects (either makes the wave wait for the load at once,
+    // which would leave one group in flight).  kVec: buffer loads of 16 bytes whose offset
+    // is moved past the end of the table for lanes past the rank or the vocabulary, where
+    // the hardware returns zeros.  Otherwise (a rank that is not a multiple of 4, or a
+    // table of 2^30 bytes or more) scalar loads from clamped addresses and selects.
+    const __amdgpu_buffer_rsrc_t brsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(TB), (short)0, (int)min((int64_t)Vt * r * 4, (int64_t)kBig), kBufWord3);
+    int boff[kTpw];
+    if constexpr (kVec) {
+#pragma unroll
+        for (int j = 0; j < kTpw; ++j) boff[j] = bok[j] ? (int)((brow[j] - TB) * 4) : kBig;
+    }
+    auto load_b = [&](int k0, int j) __attribute__((always_inline)) -> f32x4 {
+        const int k = k0 + 4 * lh;
+        f32x4 x;
+        if constexpr (kVec) {
+            const int off = k < r ? boff[j] + 4 * k : kBig;
+            x = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(brsrc, off, 0, 0));
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float raw = brow[j][min(k + e, r - 1)];
+                x[e] = (bok[j] && k + e < r) ? raw : 0.f;
+            }
+        }
+        return x;
+    };
+    // B runs kAhead slots ahead of the MFMAs.  A slot is 32 rank elements, the whole
+    // 128-byte line of every row: the 4 loads of a line leave back to back, so the line
+    // moves from L2 once (loads of one line spread over time would each fetch it again
+    // once L1 has dropped it).  Slot d of the ring holds elements kc + 32 d ..; each slot
+    // is consumed, then refilled with the slot kAhead later (the last refills of a chunk
+    // fetch the first slots of the next), so the loop carries the ring in place (a
+    // register copy of a pending load would wait for it).  The first slots are requested
+    // before anything else: they depend on nothing the setup reads.
+    static_assert(kRankChunk % (32 * kAhead) == 0, "the ring depth divides the rank chunk");
+    f32x4 ring[kAhead][kTpw][4];
+#pragma unroll
+    for (int d = 0; d < kAhead; ++d)
+#pragma unroll
+        for (int j = 0; j < kTpw; ++j)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) ring[d][j][t] = load_b(32 * d + 8 * t, j);
 
     if (tid < kGroup) {
         int m = -1;
@@ -97,90 +166,108 @@ __global__ void __launch_bounds__(kThreads) dense_pos_kernel(
         mrow[tid] = m;
     }
     __syncthreads();
-    // the B rows of this lane's vocab ids in the wave's two tiles
-    const int vt0 = blockIdx.x * kThreads + w * 64;   // first id of the wave's tiles
-    const float* brow[2];
-    bool bok[2];
+    // the logits of the epilogue (row of request lr, ids 8 c + 4 lh .. + 3 of every tile),
+    // loaded now so that they arrive while the MFMAs run; the addresses are clamped into
+    // the buffer and lanes without a valid (row, id) are masked in the epilogue
+    const int myrow = mrow[lr];
+    f32x4 zpre[kTpw][4];
+    {
+        const float* zr = logits + (int64_t)max(myrow, 0) * ldz;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int v = vt0 + 32 * j + lr;
-        bok[j] = v < V;
-        int64_t t = bok[j] ? target_of(v, d2t) : 0;
-        t = t < 0 ? 0 : (t >= Vt ? (int64_t)Vt - 1 : t);
-        brow[j] = TB + t * r;
+        for (int j = 0; j < kTpw; ++j)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int id4 = min(vt0 + 32 * j + 8 * c + 4 * lh, (int)ldz - 4);
+                zpre[j][c] = *reinterpret_cast<const f32x4*>(zr + id4);
+            }
     }
 
-    f32x16 acc[2] = {f32x16{}, f32x16{}};
-    const bool vec = (r & 3) == 0 && (reinterpret_cast<uintptr_t>(tables) & 15) == 0;
-    auto load_b = [&](int k0, int j) __attribute__((always_inline)) -> f32x4 {
-        const int k = k0 + 4 * lh;
-        f32x4 x = {0.f, 0.f, 0.f, 0.f};
-        if (vec) {
-            if (bok[j] && k < r) x = *reinterpret_cast<const f32x4*>(brow[j] + k);
-        } else {
+    f32x16 acc[kTpw];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) x[e] = (bok[j] && k + e < r) ? brow[j][k + e] : 0.f;
-        }
-        return x;
-    };
-    auto step = [&](int kc, const f32x4 (&bv)[2]) __attribute__((always_inline)) {
-        const f32x4 av = *reinterpret_cast<const f32x4*>(&As[lr * kAStride + kc + 4 * lh]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            acc[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[e], bv[0][e], acc[0], 0, 0, 0);
-            acc[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[e], bv[1][e], acc[1], 0, 0, 0);
-        }
-    };
+    for (int j = 0; j < kTpw; ++j) acc[j] = f32x16{};
     for (int c0 = 0; c0 < r; c0 += kRankChunk) {
         const int cn = min(kRankChunk, r - c0);
-        const int cpad = (cn + 15) / 16 * 16;
+        const int cpad = (cn + 31) / 32 * 32;   // <= kRankChunk, a multiple of the 32-element slot
         __syncthreads();   // the previous chunk's reads are done
-        for (int e = tid; e < kGroup * cpad; e += kThreads) {
-            const int q = e / cpad, i = e % cpad;
-            As[q * kAStride + i] = (mrow[q] >= 0 && i < cn) ? TA[arow[q] + c0 + i] : 0.f;
+        if (kVec && cn == kRankChunk) {
+            // a whole chunk: every thread issues its 8 loads of 16 bytes at once
+            constexpr int kPer = kGroup * kRankChunk / 4 / kThreads;
+            f32x4 av[kPer];
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) {
+                const int e = tid + kThreads * i, q = e / (kRankChunk / 4), c4 = e % (kRankChunk / 4);
+                av[i] = *reinterpret_cast<const f32x4*>(TA + arow[q] + c0 + 4 * c4);
+            }
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) {
+                const int e = tid + kThreads * i, q = e / (kRankChunk / 4), c4 = e % (kRankChunk / 4);
+                const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+                *reinterpret_cast<f32x4*>(&As[q * kAStride + 4 * c4]) = mrow[q] >= 0 ? av[i] : zero;
+            }
+        } else {
+            for (int e = tid; e < kGroup * cpad; e += kThreads) {
+                const int q = e / cpad, i = e % cpad;
+                As[q * kAStride + i] = (mrow[q] >= 0 && i < cn) ? TA[arow[q] + c0 + i] : 0.f;
+            }
         }
         __syncthreads();
-        // B runs two 8-element groups ahead of the MFMAs
-        f32x4 b0[2] = {load_b(c0, 0), load_b(c0, 1)};
-        f32x4 b1[2] = {load_b(c0 + 8, 0), load_b(c0 + 8, 1)};
-        for (int kc = 0; kc < cpad; kc += 16) {
-            const f32x4 b2[2] = {load_b(c0 + kc + 16, 0), load_b(c0 + kc + 16, 1)};
-            step(kc, b0);
-            const f32x4 b3[2] = {load_b(c0 + kc + 24, 0), load_b(c0 + kc + 24, 1)};
-            step(kc + 8, b1);
-            b0[0] = b2[0]; b0[1] = b2[1];
-            b1[0] = b3[0]; b1[1] = b3[1];
+        // the A operand is read from LDS one 8-element group ahead (groups alternate
+        // between avr[0] and avr[1]; a slot holds 4 groups, so the loop carries avr[0])
+        const float* arow_lds = &As[lr * kAStride + 4 * lh];
+        f32x4 avr[2];
+        avr[0] = *reinterpret_cast<const f32x4*>(arow_lds);
+        for (int kc = 0; kc < cpad; kc += 32 * kAhead) {
+#pragma unroll
+            for (int d = 0; d < kAhead; ++d) {
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    // the next 8-element group of A (past the chunk's end: a valid LDS
+                    // address, value unused); groups alternate between avr[0] and avr[1]
+                    avr[(t + 1) & 1] =
+                        *reinterpret_cast<const f32x4*>(arow_lds + min(kc + 32 * d + 8 * (t + 1), cpad - 8));
+                    __builtin_amdgcn_sched_barrier(0);   // issued before this group's MFMAs
+                    const f32x4 av = avr[t & 1];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+#pragma unroll
+                        for (int j = 0; j < kTpw; ++j)
+                            acc[j] = __builtin_amdgcn_mfma_f32_32x32x2f32(ring[d][j][t][e], av[e], acc[j], 0, 0, 0);
+                }
+#pragma unroll
+                for (int j = 0; j < kTpw; ++j)
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        ring[d][j][t] = load_b(c0 + kc + 32 * (d + kAhead) + 8 * t, j);
+                __builtin_amdgcn_sched_barrier(0);   // keep the refill here, not clustered at the end
+            }
         }
     }
 
-    // x = f(z) + bias per (request, id); per request the best (x, lowest id) of the block
-    uint64_t e16[16];
+    // x = f(z) + bias of request lr at the lane's ids, ascending (tile j, register i); the
+    // lane keeps the largest x and, on a tie, the first (lowest) id
+    const HeadMap hm = head_map(scale, cap);
+    float bx = -INFINITY;
+    uint32_t bid = 0xFFFFFFFFu;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int q = 8 * (i / 4) + 4 * lh + i % 4;
-        const int m = q < ng ? mrow[q] : -1;
-        uint64_t best_e = 0;
+    for (int j = 0; j < kTpw; ++j)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int v = vt0 + 32 * j + lr;
-            if (m >= 0 && v < V) {
-                const float x = head_scale_cap(logits[(int64_t)m * ldz + v], scale, cap) + acc[j][i];
-                const uint64_t en = pack_entry(float_to_key(x), (uint32_t)v);
-                best_e = en > best_e ? en : best_e;
+        for (int i = 0; i < 16; ++i) {
+            const int v = vt0 + 32 * j + 8 * (i / 4) + 4 * lh + i % 4;
+            const float x = head_apply(hm, zpre[j][i / 4][i % 4]) + acc[j][i];
+            if (v < V && x > bx) {
+                bx = x;
+                bid = (uint32_t)v;
             }
         }
-        // max over the 32 lanes that share lh (the 32 ids of the tile)
-        for (int o = 16; o > 0; o >>= 1) {
-            const uint64_t o2 = ((uint64_t)(uint32_t)__shfl_xor((int)(uint32_t)(best_e >> 32), o) << 32) |
-                                (uint64_t)(uint32_t)__shfl_xor((int)(uint32_t)best_e, o);
-            best_e = o2 > best_e ? o2 : best_e;
-        }
-        e16[i] = best_e;
+    // the two halves hold interleaved ids of the same request: keep the larger x, the
+    // lower id on a tie
+    const float ox = __shfl_xor(bx, 32);
+    const uint32_t oid = (uint32_t)__shfl_xor((int)bid, 32);
+    if (ox > bx || (ox == bx && oid < bid)) {
+        bx = ox;
+        bid = oid;
     }
-    if (lr == 0) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) wbest[w][8 * (i / 4) + 4 * lh + i % 4] = e16[i];
-    }
+    if (lh == 0) wbest[w][lr] = (myrow >= 0 && bid != 0xFFFFFFFFu) ? pack_entry(float_to_key(bx), bid) : 0ull;
     __syncthreads();
     if (tid < ng && mrow[tid] >= 0) {
         uint64_t bb = wbest[0][tid];
@@ -217,10 +304,17 @@ hipError_t launch_dense_walk(const float* logits, int64_t ldz, const int64_t* d2
     hipLaunchKernelGGL(dense_clear_kernel, dim3((nb + kThreads - 1) / kThreads), dim3(kThreads), 0, s, best, nb);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const dim3 grid((V + kThreads - 1) / kThreads, (R + kGroup - 1) / kGroup);
+    const dim3 grid((V + kIds - 1) / kIds, (R + kGroup - 1) / kGroup);
+    // the buffer path: 16-byte rows and a B table below 2^30 bytes (offsets stay below kBig)
+    const bool vec = (r & 3) == 0 && (reinterpret_cast<uintptr_t>(tables) & 15) == 0 &&
+                     (int64_t)Vt * r * 4 < (int64_t)kBig;
     for (int p = 0; p < L; ++p) {
-        hipLaunchKernelGGL(dense_pos_kernel, grid, dim3(kThreads), 0, s, logits, ldz, d2t, tables, last_tok,
-                           row_offsets, R, L, M, V, Vt, r, scale, cap, p, best);
+        if (vec)
+            hipLaunchKernelGGL(dense_pos_kernel<true>, grid, dim3(kThreads), 0, s, logits, ldz, d2t, tables,
+                               last_tok, row_offsets, R, L, M, V, Vt, r, scale, cap, p, best);
+        else
+            hipLaunchKernelGGL(dense_pos_kernel<false>, grid, dim3(kThreads), 0, s, logits, ldz, d2t, tables,
+                               last_tok, row_offsets, R, L, M, V, Vt, r, scale, cap, p, best);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     hipLaunchKernelGGL(dense_finish_kernel, dim3((nb + kThreads - 1) / kThreads), dim3(kThreads), 0, s, best, d2t,

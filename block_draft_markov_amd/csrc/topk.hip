@@ -469,12 +469,9 @@ hipError_t launch_topk(const float* logits, int64_t ldz, const float* lse, const
 }
 
 // ---------------------------------------------------------------- head-less argmax
-// f(z) = cap tanh(scale z / cap) (cap > 0) or scale z is non-decreasing, so every
-// logit with f(z) = max f lies in a tile whose maximum m_t has f(m_t) = max f:
-// with tile maxima only those tiles are read.  Ties go to the lowest id.
-__device__ __forceinline__ float scale_cap(float x, float scale, float cap) {
-    return cap > 0.f ? cap * tanhf(scale * x / cap) : scale * x;
-}
+// f(z) = cap tanh(scale z / cap) (cap > 0) or scale z, as head_apply computes it, is
+// non-decreasing, so every logit with f(z) = max f lies in a tile whose maximum m_t has
+// f(m_t) = max f: with tile maxima only those tiles are read.  Ties go to the lowest id.
 
 // (value, id) with the larger value, the lower id on a tie.
 __device__ __forceinline__ void better(float& v, int& i, float v2, int i2) {
@@ -493,6 +490,7 @@ __global__ void __launch_bounds__(kThreads) argmax_kernel(const float* __restric
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int m = blockIdx.x;
     const float* row = logits + (int64_t)m * ldz;
+    const HeadMap hm = head_map(scale, cap);
     float bv = -INFINITY;
     int bi = 0x7fffffff;
     // block-wide (max, lowest id)
@@ -522,7 +520,7 @@ __global__ void __launch_bounds__(kThreads) argmax_kernel(const float* __restric
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int v = base + tid + kThreads * i;
-                if (v < V) better(bv, bi, scale_cap(zv[i], scale, cap), v);
+                if (v < V) better(bv, bi, head_apply(hm, zv[i]), v);
             }
         }
         reduce();
@@ -541,7 +539,7 @@ __global__ void __launch_bounds__(kThreads) argmax_kernel(const float* __restric
         for (int i = 0; i < kTPT; ++i) {
             const int t = tid + kThreads * i;
             if (t < tiles) {
-                const float f = scale_cap(tv[i], scale, cap);
+                const float f = head_apply(hm, tv[i]);
                 tf[t] = f;
                 better(bv, bi, f, t);
             }
@@ -571,7 +569,7 @@ __global__ void __launch_bounds__(kThreads) argmax_kernel(const float* __restric
                 for (int i = 0; i < 8; ++i) {
                     const int e = base + tid + kThreads * i;
                     const int v = e < nsel * 32 ? sel[e >> 5] * 32 + (e & 31) : V;
-                    if (v < V && scale_cap(zv[i], scale, cap) == fmax) atomicMin(&s_best, v);
+                    if (v < V && head_apply(hm, zv[i]) == fmax) atomicMin(&s_best, v);
                 }
             }
             __syncthreads();
