@@ -36,6 +36,10 @@ The pages fix no scoring formula.  The one used here (stated once):
                                                       s_p = t_{m(p-1)}[c_{p-1}]
   Viterbi: the path of maximal Score; at every max the lowest slot wins.
   Greedy:  c_p = lowest argmax_k u_p[k] + pi_p(s_p, k), position by position.
+  Sampled: c_p drawn from the row x_p[k] = (u_p[k] + pi_p(s_p, k)) / T with one
+           double uniform per position: float weights exp(x - max x), running and
+           total sums in double, the smallest k whose running sum exceeds U * total
+           (see `sampled`); q_p = weights / total is the recorded proposal.
 
 Readings where the pages are silent (each listed in the design notes):
   * the gate of a transition uses the hidden state of the row that produced
@@ -289,11 +293,71 @@ def bruteforce(u: np.ndarray, S: Sequence[np.ndarray]):
     return paths[pick].copy(), float(scores[pick]), margin
 
 
+@dataclass
+class SampledWalk:
+    path: np.ndarray      # int64 [L] drawn slots
+    q: np.ndarray         # float64 [L, K] the distribution each slot was drawn from
+    score: float          # Score(c) of the drawn path (no temperature)
+    gaps: np.ndarray      # float64 [L] distance of U * total to the nearest slot boundary, / total
+
+
+def sampled(u: np.ndarray, S: Sequence[np.ndarray], uniforms: np.ndarray, temperature: float = 1.0) -> SampledWalk:
+    """Sampled walk of one request through its lattice.
+
+    [G] commit "DFlash-2 Markov head / BlockRowSource": a sampled request walks
+    the lattice with the request's draft RNG, drawing every position from the
+    lattice row after the token drawn before; the sampled-drafting commits of
+    [G] fix the arithmetic of a draw: the weights come from a float exp, their
+    running and total sums are doubles, the uniform is a double, and the
+    proposal q is recorded normalized in double for the target's rejection
+    sampling.  The random numbers are inputs (one double uniform in [0, 1)
+    per position), so the walk is a function of them.
+
+    At position p (c_{-1} selects row 0 of S_0):
+      x_k   = fp32(fp32(u_p[k] + S_p[c_{p-1}, k]) / T)    the row drawn from, in fp32
+      w_k   = fp32(exp(x_k - max_j x_j))                   float exp, correctly rounded
+      W_k   = w_0 + ... + w_k in double, in slot order;   total = W_{K-1}
+      c_p   = the smallest k with U_p * total < W_k
+      q_p   = w / total (double)
+    """
+    u32 = np.asarray(u, dtype=np.float32)
+    L, K = u32.shape
+    T = np.float32(temperature)
+    path = np.zeros(L, np.int64)
+    q = np.zeros((L, K))
+    gaps = np.zeros(L)
+    prev = 0
+    for p in range(L):
+        row = np.asarray(S[p], dtype=np.float32)[prev]
+        x = (u32[p] + row) / T                                   # float32 arithmetic
+        w = np.exp((x - x.max()).astype(np.float64)).astype(np.float32)
+        total = 0.0
+        for k in range(K):
+            total += float(w[k])
+        thr = float(uniforms[p]) * total
+        c, run = K - 1, 0.0
+        bounds = []
+        for k in range(K):
+            run += float(w[k])
+            bounds.append(run)
+            if thr < run:
+                c = k
+                break
+        # distance to the nearest running sum the draw compared with (a draw at U = 0 is
+        # slot 0 however the weights round, so 0 is no boundary)
+        b = np.array(bounds)
+        gaps[p] = float(np.min(np.abs(b - thr))) / total
+        q[p] = w.astype(np.float64) / total
+        path[p] = c
+        prev = c
+    return SampledWalk(path, q, path_score(u, S, path), gaps)
+
+
 # --------------------------------------------------------------------------
 # the whole draft step
 # --------------------------------------------------------------------------
 
-WALK_VITERBI, WALK_GREEDY = 0, 1
+WALK_VITERBI, WALK_GREEDY, WALK_SAMPLED = 0, 1, 2
 
 
 @dataclass
@@ -301,9 +365,11 @@ class DraftResult:
     tokens: np.ndarray        # int64 [M] drafted target ids
     scores: np.ndarray        # float64 [R] path scores
     slots: np.ndarray         # int64 [M] chosen slot per row
-    margins: np.ndarray       # float64 [R] runner-up margin (Viterbi) or smallest step gap (greedy)
+    margins: np.ndarray       # float64 [R] runner-up margin (Viterbi), smallest step gap (greedy),
+                              # smallest relative draw gap (sampled)
     cand: Candidates
     S: List[List[np.ndarray]]  # per request, per position
+    q: Optional[np.ndarray] = None   # float64 [M, K] proposals of a sampled walk
 
 
 def _offsets(R: int, M: int, row_offsets) -> np.ndarray:
@@ -317,8 +383,11 @@ def _offsets(R: int, M: int, row_offsets) -> np.ndarray:
 
 
 def walk_from_candidates(cand: Candidates, tables, hidden_bits, gate_w, last_tok,
-                         row_offsets=None, walk=WALK_VITERBI) -> DraftResult:
-    """Pairwise scores and the walk for every request, given the slots."""
+                         row_offsets=None, walk=WALK_VITERBI, uniforms=None,
+                         temperature: float = 1.0) -> DraftResult:
+    """Pairwise scores and the walk for every request, given the slots.
+
+    A sampled walk takes one uniform per row (uniforms [M])."""
     R = len(last_tok)
     M = cand.idx.shape[0]
     off = _offsets(R, M, row_offsets)
@@ -327,6 +396,7 @@ def walk_from_candidates(cand: Candidates, tables, hidden_bits, gate_w, last_tok
     slots = np.zeros(M, np.int64)
     scores = np.zeros(R)
     margins = np.full(R, np.inf)
+    qs = np.zeros(cand.idx.shape) if walk == WALK_SAMPLED else None
     S_all = []
     for r in range(R):
         a, b = int(off[r]), int(off[r + 1])
@@ -337,28 +407,35 @@ def walk_from_candidates(cand: Candidates, tables, hidden_bits, gate_w, last_tok
         S = lattice_scores(cand.tok[a:b], tables, hr, gate_w, int(last_tok[r]))
         if walk == WALK_VITERBI:
             path, score, margin = viterbi(cand.unary[a:b], S)
+        elif walk == WALK_SAMPLED:
+            sw = sampled(cand.unary[a:b], S, np.asarray(uniforms)[a:b], temperature)
+            path, score, margin = sw.path, sw.score, float(np.min(sw.gaps))
+            qs[a:b] = sw.q
         else:
             path, score, margin = greedy(cand.unary[a:b], S)
         slots[a:b] = path
         tokens[a:b] = cand.tok[a:b][np.arange(b - a), path]
         scores[r], margins[r] = score, margin
         S_all.append(S)
-    return DraftResult(tokens, scores, slots, margins, cand, S_all)
+    return DraftResult(tokens, scores, slots, margins, cand, S_all, qs)
 
 
 def draft_from_logits(z: np.ndarray, K: int, d2t, tables, hidden_bits, gate_w, last_tok,
-                      row_offsets=None, walk=WALK_VITERBI) -> DraftResult:
+                      row_offsets=None, walk=WALK_VITERBI, uniforms=None,
+                      temperature: float = 1.0) -> DraftResult:
     """Steps 2-4 from given logits (used to feed the GPU and the oracle the same logits)."""
     cand = candidates(z, K, d2t)
     return walk_from_candidates(cand, tables, hidden_bits, gate_w, last_tok, row_offsets,
-                                walk=walk)
+                                walk=walk, uniforms=uniforms, temperature=temperature)
 
 
 def draft_block(hidden_bits, lm_head_bits, d2t, tables, gate_w, last_tok, K,
-                row_offsets=None, walk=WALK_VITERBI) -> DraftResult:
+                row_offsets=None, walk=WALK_VITERBI, uniforms=None,
+                temperature: float = 1.0) -> DraftResult:
     """The whole draft step: hidden states of the packed block rows -> drafted tokens."""
     z = logits(hidden_bits, lm_head_bits)
-    return draft_from_logits(z, K, d2t, tables, hidden_bits, gate_w, last_tok, row_offsets, walk)
+    return draft_from_logits(z, K, d2t, tables, hidden_bits, gate_w, last_tok, row_offsets, walk,
+                             uniforms, temperature)
 
 
 # --------------------------------------------------------------------------
