@@ -134,6 +134,11 @@ def main():
                                           soft_cap=30.0, workspace=ws, with_values=False, out=(nh_tok, None)),
                   args.steps, 3)
     log(f"dense walk step (scale 1, soft cap 30): {dn_ms * 1e3:.1f} us")
+    # ---- the whole step with the sampled walk (one seeded double uniform per row), timed alone
+    uni = torch.rand(M, dtype=torch.float64, device="cuda", generator=torch.Generator("cuda").manual_seed(11))
+    sp_ms = timed(lambda: api.draft_block_sampled(hidden, W, tables, last_tok, uni, top_k=K, temperature=1.0, d2t=d2t,
+                                                  gate_w=gate_w, block_len=L, workspace=ws), args.steps, 3)
+    log(f"sampled-walk step (temperature 1): {sp_ms * 1e3:.1f} us")
     log(f"stages: lm_head {k1_ms * 1e3:.1f} us, top-k {k2_ms * 1e3:.1f} us, pair {k3_ms * 1e3:.1f} us, "
         f"walk {k4_ms * 1e3:.1f} us")
 
@@ -194,6 +199,8 @@ def main():
                        "out_scale": 1.0, "soft_cap": 30.0,
                        # per position: the gathered B rows of every draft id and the rows' logits
                        "bytes_per_position": Vd * r * 4 + R * Vd * 4},
+        "sampled_step": {"us": round(sp_ms * 1e3, 2), "blocks_per_s": round(R / (sp_ms * 1e-3), 1),
+                         "temperature": 1.0},
         "standalone_stages_us": {"lm_head": round(k1_ms * 1e3, 2), "topk": round(k2_ms * 1e3, 2),
                       "pair_scores": round(k3_ms * 1e3, 2), "walk": round(k4_ms * 1e3, 2)},
     }

@@ -50,6 +50,9 @@ SIGNATURES = {
     "dflash_draft_argmax": (ctypes.c_int, [_PD, _P, _P, _P, ctypes.c_float, ctypes.c_float, _P, _P, _P, _SZ, _P]),
     "dflash_draft_dense": (ctypes.c_int, [_PD, _P, _P, _P, _P, _P, _P, ctypes.c_float, ctypes.c_float, _P, _P, _P,
                                           _SZ, _P]),
+    "dflash_draft_block_sampled": (ctypes.c_int, [_PD, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P,
+                                                  _P, _SZ, _P]),
+    "dflash_walk_sampled": (ctypes.c_int, [_PD, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P, _P, _P]),
     "dflash_check_d2t": (ctypes.c_int, [_P, _I32, _I32, ctypes.POINTER(ctypes.c_int)]),
     "dflash_last_error": (ctypes.c_char_p, []),
 }

@@ -118,6 +118,34 @@ def draft_block(hidden: torch.Tensor, lm_head_w: torch.Tensor, tables: torch.Ten
     return tokens, scores
 
 
+def draft_block_sampled(hidden: torch.Tensor, lm_head_w: torch.Tensor, tables: torch.Tensor,
+                        last_tok: torch.Tensor, uniforms: torch.Tensor, *, top_k: int, temperature: float = 1.0,
+                        d2t: Optional[torch.Tensor] = None, gate_w: Optional[torch.Tensor] = None,
+                        row_offsets: Optional[torch.Tensor] = None, block_len: Optional[int] = None,
+                        workspace: Optional[Workspace] = None, with_q: bool = True):
+    """The whole step with the sampled walk: (tokens int64 [M], scores fp32 [R], q float64 [M, K] or None)."""
+    _bf16(hidden, "hidden"), _bf16(lm_head_w, "lm_head")
+    _expect(tables, torch.float32, "tables"), _expect(last_tok, torch.int64, "last_tok")
+    _expect(d2t, torch.int64, "d2t"), _expect(gate_w, torch.float32, "gate_w")
+    _expect(row_offsets, torch.int32, "row_offsets"), _expect(uniforms, torch.float64, "uniforms")
+    M, H = hidden.shape
+    Vd = lm_head_w.shape[0]
+    Vt, r = tables.shape[1], tables.shape[2]
+    R = last_tok.shape[0]
+    L = block_len if block_len is not None else (M // R if R else 1)
+    d = make_dims(R=R, L=L, M=M, H=H, Vd=Vd, Vt=Vt, K=top_k, r=r)
+    dev = hidden.device
+    tokens = torch.empty(M, dtype=torch.int64, device=dev)
+    scores = torch.empty(R, dtype=torch.float32, device=dev)
+    q = torch.empty((M, top_k), dtype=torch.float64, device=dev) if with_q else None
+    wsp, wsn = _ws(workspace, dev).get(workspace_bytes(d))
+    check(load().dflash_draft_block_sampled(ctypes.byref(d), _ptr(hidden), _ptr(lm_head_w), _ptr(d2t), _ptr(tables),
+                                            _ptr(gate_w), _ptr(last_tok), _ptr(row_offsets), _ptr(uniforms),
+                                            float(temperature), _ptr(tokens), _ptr(scores), _ptr(q), wsp, wsn,
+                                            _stream(dev)))
+    return tokens, scores, q
+
+
 def draft_argmax(hidden: torch.Tensor, lm_head_w: torch.Tensor, *, d2t: Optional[torch.Tensor] = None,
                  target_vocab: Optional[int] = None, out_scale: float = 1.0, soft_cap: float = 0.0,
                  workspace: Optional[Workspace] = None, with_values: bool = True,
@@ -252,6 +280,27 @@ def walk(cand_tok: torch.Tensor, unary: torch.Tensor, pair: torch.Tensor, R: int
     check(load().dflash_walk(ctypes.byref(d), _ptr(cand_tok), _ptr(unary), _ptr(pair), _ptr(row_offsets),
                              _ptr(tokens), _ptr(scores), _ptr(slots), _stream(dev)))
     return tokens, scores, slots
+
+
+def walk_sampled(cand_tok: torch.Tensor, unary: torch.Tensor, pair: torch.Tensor, R: int, uniforms: torch.Tensor, *,
+                 temperature: float = 1.0, row_offsets: Optional[torch.Tensor] = None,
+                 block_len: Optional[int] = None, with_q: bool = True):
+    """Part 4, sampled: (tokens int64 [M], scores fp32 [R], slots int32 [M], q float64 [M, K] or None)."""
+    _expect(cand_tok, torch.int64, "cand_tok"), _expect(unary, torch.float32, "unary")
+    _expect(pair, torch.float32, "pair"), _expect(row_offsets, torch.int32, "row_offsets")
+    _expect(uniforms, torch.float64, "uniforms")
+    M, K = cand_tok.shape
+    L = block_len if block_len is not None else (M // R if R else 1)
+    d = make_dims(R=R, L=L, M=M, H=8, Vd=K, K=K)
+    dev = cand_tok.device
+    tokens = torch.empty(M, dtype=torch.int64, device=dev)
+    scores = torch.empty(R, dtype=torch.float32, device=dev)
+    slots = torch.empty(M, dtype=torch.int32, device=dev)
+    q = torch.empty((M, K), dtype=torch.float64, device=dev) if with_q else None
+    check(load().dflash_walk_sampled(ctypes.byref(d), _ptr(cand_tok), _ptr(unary), _ptr(pair), _ptr(row_offsets),
+                                     _ptr(uniforms), float(temperature), _ptr(tokens), _ptr(scores), _ptr(slots),
+                                     _ptr(q), _stream(dev)))
+    return tokens, scores, slots, q
 
 
 def check_d2t(d2t_host, Vd: int, Vt: int) -> bool:

@@ -139,22 +139,11 @@ T* at(void* ws, size_t off) {
     return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
 }
 
-}  // namespace
-
-extern "C" {
-
-size_t dflash_workspace_bytes(const dflash_dims* dims) {
-    if (check_dims(dims) != DFLASH_OK) return 0;
-    ok();
-    return layout(dims).total;
-}
-
-int64_t dflash_logits_stride(int32_t draft_vocab) { return draft_vocab < 0 ? 0 : round_up(draft_vocab, 4); }
-
-int dflash_draft_block(const dflash_dims* d, const uint16_t* hidden, const uint16_t* lm_head, const int64_t* d2t,
-                       const float* tables, const float* gate_w, const int64_t* last_tok,
-                       const int32_t* row_offsets, int64_t* tokens, float* scores, void* ws, size_t ws_bytes,
-                       void* stream) {
+// Parts 1-3 of a whole step (validation, then lm_head, Top-K and pair scores);
+// the caller launches the walk.
+int lattice_stages(const dflash_dims* d, const uint16_t* hidden, const uint16_t* lm_head, const int64_t* d2t,
+                   const float* tables, const float* gate_w, const int64_t* last_tok, const int32_t* row_offsets,
+                   int64_t* tokens, float* scores, void* ws, size_t ws_bytes, void* stream, Layout& l) {
     int rc;
     if ((rc = check_dims(d)) || (rc = check_rows(d, row_offsets))) return rc;
     const int64_t M = d->total_rows, R = d->num_requests;
@@ -170,7 +159,6 @@ int dflash_draft_block(const dflash_dims* d, const uint16_t* hidden, const uint1
                                          "not supported");
     if (!aligned(hidden, 16) || !aligned(lm_head, 16))
         return fail(DFLASH_EINVAL, "hidden and lm_head must be 16-byte aligned");
-    Layout l;
     if ((rc = check_ws(d, ws, ws_bytes, l))) return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
@@ -193,10 +181,62 @@ int dflash_draft_block(const dflash_dims* d, const uint16_t* hidden, const uint1
                                         d->num_requests, d->block_len, d->total_rows, d->hidden, d->target_vocab,
                                         d->top_k, d->rank, at<float>(ws, l.pair), s)) != hipSuccess)
         return hip_fail(e, "pair-score launch");
+    return DFLASH_OK;
+}
+
+// The sampled walk's own arguments: a uniform per row, a finite positive temperature.
+int check_sampling(const dflash_dims* d, const double* uniforms, float temperature) {
+    if (!(temperature > 0.f) || !std::isfinite(temperature))
+        return fail(DFLASH_EINVAL, "temperature = %g must be finite and positive", (double)temperature);
+    return need(uniforms, d->total_rows, "uniforms");
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t dflash_workspace_bytes(const dflash_dims* dims) {
+    if (check_dims(dims) != DFLASH_OK) return 0;
+    ok();
+    return layout(dims).total;
+}
+
+int64_t dflash_logits_stride(int32_t draft_vocab) { return draft_vocab < 0 ? 0 : round_up(draft_vocab, 4); }
+
+int dflash_draft_block(const dflash_dims* d, const uint16_t* hidden, const uint16_t* lm_head, const int64_t* d2t,
+                       const float* tables, const float* gate_w, const int64_t* last_tok,
+                       const int32_t* row_offsets, int64_t* tokens, float* scores, void* ws, size_t ws_bytes,
+                       void* stream) {
+    int rc;
+    Layout l;
+    if ((rc = lattice_stages(d, hidden, lm_head, d2t, tables, gate_w, last_tok, row_offsets, tokens, scores, ws,
+                             ws_bytes, stream, l)))
+        return rc;
+    hipError_t e;
     if ((e = dflash::launch_walk(at<int64_t>(ws, l.ctok), at<float>(ws, l.unary), at<float>(ws, l.pair),
                                  row_offsets, d->num_requests, d->block_len, d->total_rows, d->top_k, d->walk,
-                                 tokens, scores, nullptr, s)) != hipSuccess)
+                                 tokens, scores, nullptr, static_cast<hipStream_t>(stream))) != hipSuccess)
         return hip_fail(e, "walk launch");
+    return ok();
+}
+
+int dflash_draft_block_sampled(const dflash_dims* d, const uint16_t* hidden, const uint16_t* lm_head,
+                               const int64_t* d2t, const float* tables, const float* gate_w,
+                               const int64_t* last_tok, const int32_t* row_offsets, const double* uniforms,
+                               float temperature, int64_t* tokens, float* scores, double* q, void* ws,
+                               size_t ws_bytes, void* stream) {
+    int rc;
+    if ((rc = check_dims(d)) || (rc = check_sampling(d, uniforms, temperature))) return rc;
+    Layout l;
+    if ((rc = lattice_stages(d, hidden, lm_head, d2t, tables, gate_w, last_tok, row_offsets, tokens, scores, ws,
+                             ws_bytes, stream, l)))
+        return rc;
+    hipError_t e;
+    if ((e = dflash::launch_walk_sampled(at<int64_t>(ws, l.ctok), at<float>(ws, l.unary), at<float>(ws, l.pair),
+                                         row_offsets, d->num_requests, d->block_len, d->total_rows, d->top_k,
+                                         uniforms, temperature, tokens, scores, nullptr, q,
+                                         static_cast<hipStream_t>(stream))) != hipSuccess)
+        return hip_fail(e, "sampled walk launch");
     return ok();
 }
 
@@ -357,6 +397,23 @@ int dflash_walk(const dflash_dims* d, const int64_t* cand_tok, const float* unar
                                        d->total_rows, d->top_k, d->walk, tokens, scores, slots,
                                        static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "walk launch");
+    return ok();
+}
+
+int dflash_walk_sampled(const dflash_dims* d, const int64_t* cand_tok, const float* unary, const float* pair,
+                        const int32_t* row_offsets, const double* uniforms, float temperature, int64_t* tokens,
+                        float* scores, int32_t* slots, double* q, void* stream) {
+    int rc;
+    if ((rc = check_dims(d)) || (rc = check_rows(d, row_offsets))) return rc;
+    if ((rc = check_sampling(d, uniforms, temperature))) return rc;
+    const int64_t M = d->total_rows, R = d->num_requests;
+    if ((rc = need(cand_tok, M, "cand_tok")) || (rc = need(unary, M, "unary")) || (rc = need(pair, M, "pair")) ||
+        (rc = need(tokens, M, "tokens")) || (rc = need(scores, R, "scores")))
+        return rc;
+    hipError_t e = dflash::launch_walk_sampled(cand_tok, unary, pair, row_offsets, d->num_requests, d->block_len,
+                                               d->total_rows, d->top_k, uniforms, temperature, tokens, scores,
+                                               slots, q, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "sampled walk launch");
     return ok();
 }
 

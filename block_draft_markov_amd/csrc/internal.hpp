@@ -57,5 +57,11 @@ hipError_t launch_dense_walk(const float* logits, int64_t ldz, const int64_t* d2
 hipError_t launch_walk(const int64_t* cand_tok, const float* unary, const float* pair,
                        const int32_t* row_offsets, int R, int L, int M, int K, int walk,
                        int64_t* tokens, float* scores, int32_t* slots, hipStream_t s);
+// The sampled walk: one double uniform per row, temperature > 0; q [M][K] (or NULL)
+// receives the proposal of every row.
+hipError_t launch_walk_sampled(const int64_t* cand_tok, const float* unary, const float* pair,
+                               const int32_t* row_offsets, int R, int L, int M, int K, const double* uniforms,
+                               float temperature, int64_t* tokens, float* scores, int32_t* slots, double* q,
+                               hipStream_t s);
 
 }  // namespace dflash

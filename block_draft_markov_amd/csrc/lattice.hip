@@ -20,7 +20,11 @@
 // thread (k, q) takes the best delta(j) + S[j][k] over j in its quarter q of
 // the slots (ascending, strict >), and the quarters are combined in order, so
 // the lowest j wins a tie; back-pointers stay in LDS.  Greedy: one wave, an
-// argmax per position (DPP max reduction, lowest lane of a ballot).
+// argmax per position (DPP max reduction, lowest lane of a ballot).  Sampled
+// (same commit: a sampled request walks the lattice with its draft RNG; the
+// sampled-drafting commits: float weights, double sums, a double uniform, the
+// proposal recorded for rejection sampling): one wave; per position the row
+// after the slot drawn before, one caller-supplied uniform per row.
 
 #include "common.hpp"
 #include "internal.hpp"
@@ -162,15 +166,17 @@ __global__ void __launch_bounds__(kPairThreads) pair_scores_kernel(
 }
 
 constexpr int kWalkThreads = 256;
+constexpr int kWalkSampled = 2;   // the sampled walk (its own entry points; not a dims.walk value)
 constexpr int kWalkChunk = 4;     // positions of S and u per LDS buffer; two buffers
 
 __global__ void __launch_bounds__(kWalkThreads) walk_kernel(const int64_t* __restrict__ cand_tok,
                                                             const float* __restrict__ unary,
                                                             const float* __restrict__ pair,
                                                             const int32_t* __restrict__ row_offsets, int L, int M,
-                                                            int K, int walk, int64_t* __restrict__ tokens,
+                                                            int K, int walk, const double* __restrict__ uniforms,
+                                                            float temperature, int64_t* __restrict__ tokens,
                                                             float* __restrict__ scores,
-                                                            int32_t* __restrict__ slots) {
+                                                            int32_t* __restrict__ slots, double* __restrict__ qprob) {
     __shared__ __attribute__((aligned(16))) float Ss[2][kWalkChunk][64 * 64];
     __shared__ float Us[2][kWalkChunk][64];
     __shared__ float qbest[2][4][64];
@@ -265,6 +271,33 @@ __global__ void __launch_bounds__(kWalkThreads) walk_kernel(const int64_t* __res
                     if (q == 0) back[p][lane] = (uint8_t)min(ar, K - 1);
                     par ^= 1;
                 }
+            } else if (walk == kWalkSampled) {
+                if (tid < 64) {
+                    // the row after the slot drawn before, in fp32; float weights (the fp32
+                    // rounding of exp, taken in double); running and total sums in double in
+                    // slot order; the smallest slot whose running sum exceeds U * total
+                    const float v = act ? Us[buf][pp][lane] + Ss[buf][pp][prev * 64 + lane] : -INFINITY;
+                    const float xs = act ? v / temperature : -INFINITY;
+                    const float mx = wave_max(xs);
+                    const float wf = act ? (float)exp((double)(xs - mx)) : 0.f;
+                    double tot = 0.0;
+                    for (int k = 0; k < K; ++k)
+                        tot += (double)__int_as_float(__builtin_amdgcn_readlane(__float_as_int(wf), k));
+                    const double thr = uniforms[a + p] * tot;
+                    int c = K - 1;
+                    double run = 0.0;
+                    for (int k = 0; k < K; ++k) {
+                        run += (double)__int_as_float(__builtin_amdgcn_readlane(__float_as_int(wf), k));
+                        if (thr < run) {
+                            c = k;
+                            break;
+                        }
+                    }
+                    if (qprob && act) qprob[(int64_t)(a + p) * K + lane] = (double)wf / tot;
+                    total += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), c));
+                    if (lane == 0) path[p] = c;
+                    prev = c;
+                }
             } else if (tid < 64) {
                 const float v = act ? Us[buf][pp][lane] + Ss[buf][pp][prev * 64 + lane] : -INFINITY;
                 const float mx = wave_max(v);
@@ -323,7 +356,17 @@ hipError_t launch_walk(const int64_t* cand_tok, const float* unary, const float*
                        hipStream_t s) {
     if (R <= 0) return hipSuccess;
     hipLaunchKernelGGL(walk_kernel, dim3(R), dim3(kWalkThreads), 0, s, cand_tok, unary, pair, row_offsets, L, M, K,
-                       walk, tokens, scores, slots);
+                       walk, nullptr, 1.f, tokens, scores, slots, nullptr);
+    return hipGetLastError();
+}
+
+hipError_t launch_walk_sampled(const int64_t* cand_tok, const float* unary, const float* pair,
+                               const int32_t* row_offsets, int R, int L, int M, int K, const double* uniforms,
+                               float temperature, int64_t* tokens, float* scores, int32_t* slots, double* q,
+                               hipStream_t s) {
+    if (R <= 0) return hipSuccess;
+    hipLaunchKernelGGL(walk_kernel, dim3(R), dim3(kWalkThreads), 0, s, cand_tok, unary, pair, row_offsets, L, M, K,
+                       kWalkSampled, uniforms, temperature, tokens, scores, slots, q);
     return hipGetLastError();
 }
 

@@ -159,6 +159,40 @@ int dflash_walk(const dflash_dims* dims, const int64_t* cand_tok, const float* u
                 const float* pair, const int32_t* row_offsets,
                 int64_t* tokens, float* scores, int32_t* slots, void* stream);
 
+/* Sampled drafting (openvino.genai page "Add DSpark and DFlash v2 drafts and
+ * sampled drafting ...", commit "DFlash-2 Markov head / BlockRowSource": a
+ * sampled request walks the lattice with the request's draft RNG; the
+ * sampled-drafting commits of the same page: the weights are float exps, their
+ * running and total sums doubles, the uniform a double, and the proposal of
+ * every drawn candidate is recorded for the target's rejection sampling).
+ * The caller's RNG supplies the uniforms, so a draw is a function of them.
+ * For request r, position p (row m), c_{-1} selecting row 0 of S_0:
+ *   x_k = fp32(fp32(u_m[k] + S_p[c_{p-1}][k]) / temperature)
+ *   w_k = fp32(exp(x_k - max_j x_j))        (rounded from a double exp)
+ *   W_k = w_0 + ... + w_k in double, in slot order; total = W_{K-1}
+ *   c_p = the smallest k with uniforms[m] * total < W_k (K - 1 if none)
+ *   q[m][k] = w_k / total (double)
+ *   uniforms  double [M] in [0, 1), one per row
+ *   temperature finite and > 0 (DFLASH_EINVAL otherwise)
+ *   q         out double [M][K] or NULL: the proposal each slot was drawn from
+ *   scores    out fp32 [R]: Score(c) of the drawn path (as dflash_draft_block)
+ * Everything else as dflash_draft_block; dims->walk must be valid and is not
+ * used. */
+int dflash_draft_block_sampled(const dflash_dims* dims,
+                               const uint16_t* hidden, const uint16_t* lm_head,
+                               const int64_t* d2t, const float* tables, const float* gate_w,
+                               const int64_t* last_tok, const int32_t* row_offsets,
+                               const double* uniforms, float temperature,
+                               int64_t* tokens, float* scores, double* q,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* Part 4 sampled: the walk above from given candidates, unary and S (the
+ * layouts of dflash_walk); slots out int32 [M] or NULL. */
+int dflash_walk_sampled(const dflash_dims* dims, const int64_t* cand_tok, const float* unary,
+                        const float* pair, const int32_t* row_offsets,
+                        const double* uniforms, float temperature,
+                        int64_t* tokens, float* scores, int32_t* slots, double* q, void* stream);
+
 /* Head-less draft step (openvino.genai page, commit "DFlash-2 Markov head /
  * BlockRowSource": without a Markov head the selector scales and soft caps
  * the backbone rows, and a greedy request takes the best token of every row).

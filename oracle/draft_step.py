@@ -343,10 +343,11 @@ def sampled(u: np.ndarray, S: Sequence[np.ndarray], uniforms: np.ndarray, temper
             if thr < run:
                 c = k
                 break
-        # distance to the nearest running sum the draw compared with (a draw at U = 0 is
-        # slot 0 however the weights round, so 0 is no boundary)
-        b = np.array(bounds)
-        gaps[p] = float(np.min(np.abs(b - thr))) / total
+        # distance to the nearest running sum the draw compared with, relative to the total.
+        # 0 and the last running sum (the total itself) are no boundaries: U * total < total
+        # for every U < 1, and U = 0 draws slot 0, however the weights round
+        b = np.array(bounds[:K - 1])
+        gaps[p] = float(np.min(np.abs(b - thr))) / total if b.size else np.inf
         q[p] = w.astype(np.float64) / total
         path[p] = c
         prev = c

@@ -44,7 +44,7 @@ def err(lib):
 
 def test_every_declared_symbol_is_exported(lib):
     names = header_functions()
-    assert len(names) == 12, names
+    assert len(names) == 14, names
     for n in names:
         assert hasattr(lib, n), f"{n} declared in include/ but not exported"
     assert set(names) == set(bdm.SIGNATURES), "binding and header disagree"
@@ -261,3 +261,29 @@ def test_draft_dense_validates(lib):
     assert call(ws=None) == bdm.EWORKSPACE
     assert call(wsn=16) == bdm.EWORKSPACE
     assert call(d=dims(rank=0)) == bdm.EINVAL and "rank" in err(lib)
+
+
+def test_sampled_entry_points_validate(lib):
+    d = dims()
+    big = 1 << 40
+    blk = lambda **p: lib.dflash_draft_block_sampled(
+        ctypes.byref(p.get("d", d)), p.get("hidden", FAKE), FAKE, None, FAKE, None, FAKE, None,
+        p.get("uni", FAKE), p.get("temp", 1.0), p.get("tok", FAKE), p.get("sc", FAKE), None, p.get("ws", FAKE),
+        p.get("wsn", big), None)
+    assert blk(temp=0.0) == bdm.EINVAL and "temperature" in err(lib)
+    assert blk(temp=-1.0) == bdm.EINVAL and "temperature" in err(lib)
+    assert blk(temp=float("inf")) == bdm.EINVAL and "temperature" in err(lib)
+    assert blk(temp=float("nan")) == bdm.EINVAL and "temperature" in err(lib)
+    assert blk(uni=None) == bdm.EINVAL and "uniforms" in err(lib)
+    assert blk(tok=None) == bdm.EINVAL and "tokens" in err(lib)
+    assert blk(sc=None) == bdm.EINVAL and "scores" in err(lib)
+    assert blk(d=dims(top_k=0)) == bdm.EINVAL and "top_k" in err(lib)
+    assert blk(d=dims(total_rows=5)) == bdm.EINVAL and "row_offsets" in err(lib)
+    assert blk(ws=None) == bdm.EWORKSPACE
+    wlk = lambda **p: lib.dflash_walk_sampled(
+        ctypes.byref(p.get("d", d)), FAKE, FAKE, FAKE, None, p.get("uni", FAKE), p.get("temp", 1.0),
+        p.get("tok", FAKE), FAKE, None, None, None)
+    assert wlk(temp=0.0) == bdm.EINVAL and "temperature" in err(lib)
+    assert wlk(uni=None) == bdm.EINVAL and "uniforms" in err(lib)
+    assert wlk(tok=None) == bdm.EINVAL and "tokens" in err(lib)
+    assert wlk(d=dims(block_len=0, total_rows=0)) == bdm.EINVAL and "block_len" in err(lib)
