@@ -280,19 +280,16 @@ __global__ void __launch_bounds__(kWalkThreads) walk_kernel(const int64_t* __res
                     const float xs = act ? v / temperature : -INFINITY;
                     const float mx = wave_max(xs);
                     const float wf = act ? (float)exp((double)(xs - mx)) : 0.f;
-                    double tot = 0.0;
-                    for (int k = 0; k < K; ++k)
-                        tot += (double)__int_as_float(__builtin_amdgcn_readlane(__float_as_int(wf), k));
-                    const double thr = uniforms[a + p] * tot;
-                    int c = K - 1;
-                    double run = 0.0;
+                    // one sequential pass in slot order: lane k keeps the running sum W_k, and
+                    // W_{K-1} is the total; the draw is the lowest lane with U * total < W_k
+                    double run = 0.0, mine = 0.0;
                     for (int k = 0; k < K; ++k) {
                         run += (double)__int_as_float(__builtin_amdgcn_readlane(__float_as_int(wf), k));
-                        if (thr < run) {
-                            c = k;
-                            break;
-                        }
+                        mine = lane == k ? run : mine;
                     }
+                    const double tot = run;
+                    const double thr = uniforms[a + p] * tot;
+                    const int c = min(lowest_lane(act && thr < mine), K - 1);
                     if (qprob && act) qprob[(int64_t)(a + p) * K + lane] = (double)wf / tot;
                     total += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), c));
                     if (lane == 0) path[p] = c;
