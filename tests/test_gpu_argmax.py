@@ -99,3 +99,12 @@ def test_draft_argmax_qwen3_4b_batch_sampled_rows():
     say(f"argmax qwen3_4b_32: rows {rows}")
     counts = _run(inp, 1.25, 30.0, rows)
     say(f"  {counts}")
+
+
+def test_draft_argmax_pruned_ocr_sampled_rows():
+    """The pruned-vocabulary shape (d2t into 248100 targets), 12 sampled rows against the oracle."""
+    inp = di.make_inputs(di.SHAPES["pruned_ocr"])
+    rows = list(range(0, inp.M, 20))
+    say(f"argmax pruned_ocr: rows {rows}")
+    counts = _run(inp, 1.0, 30.0, rows)
+    say(f"  {counts}")

@@ -201,3 +201,15 @@ def test_draft_dense_qwen3_4b_batch_sampled_rows():
     say(f"dense qwen3_4b_32: rows {rows}")
     counts = _check(inp, inp.hidden, None, L, 1.0, 30.0, tok, val, rows=rows)
     say(f"  {counts}")
+
+
+def test_draft_dense_pruned_ocr_sampled_rows():
+    """The pruned-vocabulary shape (114688 draft ids mapped into 248100 targets, H 2048, 16 x 15 rows):
+    B rows gathered by target id through d2t, sampled rows against the oracle."""
+    inp = di.make_inputs(di.SHAPES["pruned_ocr"])
+    L = inp.shape.L
+    tok, val = _run_gpu(inp, inp.hidden, None, L, 1.0, 30.0)
+    rows = [0, 1, 14, 15 * 7 + 8, 15 * 15 + 14]
+    say(f"dense pruned_ocr: rows {rows}")
+    counts = _check(inp, inp.hidden, None, L, 1.0, 30.0, tok, val, rows=rows)
+    say(f"  {counts}")

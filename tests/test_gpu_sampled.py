@@ -190,3 +190,9 @@ def test_sampled_end_to_end_qwen3_4b_batch_sampled_requests():
     """The Qwen3-4B batch (32 requests x 7 rows), three requests checked against the oracle."""
     inp = di.make_inputs(di.SHAPES["qwen3_4b_32"])
     _sampled_end_to_end(inp, [0, 13, 31], T=1.0, seed=7)
+
+
+def test_sampled_end_to_end_dflash2_27b_sampled_requests():
+    """The gated 27B shape (16 requests x 15 rows, V 248100, H 5120), two requests against the oracle."""
+    inp = di.make_inputs(di.SHAPES["dflash2_27b"])
+    _sampled_end_to_end(inp, [0, 15], T=1.0, seed=8)
