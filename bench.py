@@ -139,6 +139,11 @@ def main():
     sp_ms = timed(lambda: api.draft_block_sampled(hidden, W, tables, last_tok, uni, top_k=K, temperature=1.0, d2t=d2t,
                                                   gate_w=gate_w, block_len=L, workspace=ws), args.steps, 3)
     log(f"sampled-walk step (temperature 1): {sp_ms * 1e3:.1f} us")
+    # ---- one request of the same workload alone (its first block: L rows, the same weights)
+    h1, lt1 = hidden[:L].contiguous(), last_tok[:1].contiguous()
+    one_ms = timed(lambda: api.draft_block(h1, W, tables, lt1, top_k=K, d2t=d2t, gate_w=gate_w, block_len=L,
+                                           walk=args.walk, workspace=ws), args.steps, 3)
+    log(f"single request ({L} rows): {one_ms * 1e3:.1f} us")
     log(f"stages: lm_head {k1_ms * 1e3:.1f} us, top-k {k2_ms * 1e3:.1f} us, pair {k3_ms * 1e3:.1f} us, "
         f"walk {k4_ms * 1e3:.1f} us")
 
@@ -185,7 +190,7 @@ def main():
                    "draft_vocab": Vd, "target_vocab": Vt, "top_k": K, "rank": r, "gated": shape.gated,
                    "pruned": shape.pruned, "walk": args.walk, "parallelism": "single GPU"},
         "rows_per_s": round(rows_per_s, 1),
-        "roofline": {"kernel": "lmhead_dma_kernel" if M > 64 else "lmhead_gemm_lse_kernel", "bound": "hbm",
+        "roofline": {"kernel": "lmhead_dma_kernel", "bound": "hbm",
                      "achieved": round(k1_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(k1_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "bytes_per_launch": k1_bytes, "avg_launch_us": round(k1_ms * 1e3, 2),
@@ -199,6 +204,8 @@ def main():
                        "out_scale": 1.0, "soft_cap": 30.0,
                        # per position: the gathered B rows of every draft id and the rows' logits
                        "bytes_per_position": Vd * r * 4 + R * Vd * 4},
+        "single_request_step": {"us": round(one_ms * 1e3, 2), "blocks_per_s": round(1 / (one_ms * 1e-3), 1),
+                                "rows": L},
         "sampled_step": {"us": round(sp_ms * 1e3, 2), "blocks_per_s": round(R / (sp_ms * 1e-3), 1),
                          "temperature": 1.0},
         "standalone_stages_us": {"lm_head": round(k1_ms * 1e3, 2), "topk": round(k2_ms * 1e3, 2),

@@ -9,10 +9,10 @@ namespace dflash {
 
 // ---------------------------------------------------------------- part 1: lm_head GEMM
 // A workgroup owns a contiguous range of vocabulary tiles and keeps one
-// (max, sum exp) partial per row (per wave for more than 64 rows).
+// (max, sum exp) partial per row and wave.
 int lmhead_partials(int M, int V);       // (max, sum exp) partials per row
-// For more than 64 rows the kernel can also store the maximum of every tile
-// of 32 logits of every row: tile_max [M][ldt], ldt >= ceil(V / 32).
+// The kernel can also store the maximum of every tile of 32 logits of every
+// row: tile_max [M][ldt], ldt >= ceil(V / 32).
 bool lmhead_has_tile_max(int M);
 hipError_t launch_lmhead(const uint16_t* hidden, const uint16_t* W, float* logits, int64_t ldz,
                          float2* lse_part, float* tile_max, int64_t ldt, int M, int H, int V, hipStream_t s);

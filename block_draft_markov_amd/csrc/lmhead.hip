@@ -11,20 +11,13 @@
 // of W, under the MI355X ridge of about 312, so it is bound by HBM; W is read
 // exactly once.
 //
-// Work split.  The vocabulary is cut into tiles of 16 rows.  Workgroup b owns
-// the contiguous tile range [b*T/G, (b+1)*T/G) and all 16*MT hidden rows of
-// its row chunk; it walks its range in passes of 4*NT tiles (NT per wave).
-// Every wave streams the W rows of its own tiles from HBM straight into MFMA
-// operand registers (no reuse across waves, so no LDS), while the hidden tile
-// that all four waves share is staged through LDS, double buffered.
-//
-// MFMA: v_mfma_f32_16x16x32_bf16 with A = W (16 vocab rows x 32 h), B = hidden
-// (32 h x 16 rows).  The reduction index only has to be paired identically in
-// A and B, so every lane loads 16 contiguous h values (two operands) per row
-// and 64-element step: lane group g (lanes 16g..16g+15) of the MFMA of
-// sub-step s covers h = k0 + 16 g + 8 s .. + 7 in both operands.  The result
-// D[i][j] of a lane is 4 consecutive vocabulary entries (i = 4 (lane / 16) + q)
-// of one row (j = lane % 16), stored as one 16-byte write.
+// One kernel for every batch size: the vocabulary is cut into tiles of 32 rows,
+// one workgroup per CU owns a contiguous tile range and all rows of its row
+// chunk, and every operand byte is staged through LDS by buffer loads that write
+// LDS directly (see the kernel's notes below).  Batches of up to 64 rows give
+// each wave one vocab tile per pass (128 W rows per workgroup and step: the W
+// stream then runs at about 5.7 TB/s); larger batches two, which halves the
+// re-reads of their hidden states.
 
 #include "common.hpp"
 #include "internal.hpp"
@@ -37,22 +30,18 @@ namespace dflash {
 
 namespace {
 
-constexpr int kThreads = 256;
 constexpr int kBK = 64;                       // h elements per stage
-constexpr int kRowBytes = kBK * 2 + 16;       // padded LDS row: conflict-free 16-byte reads
-constexpr int kNT = 4;      // vocab tiles per wave per pass of the small-row kernel
-constexpr int kDepth = 4;   // its W register ring
 
 struct LmHeadArgs {
     const uint16_t* hidden;
     const uint16_t* W;
     float* logits;
     float2* part;
-    float* tmax;     // per-tile maxima [M][ldt] or null (batched kernel only)
+    float* tmax;     // per-tile maxima [M][ldt] or null
     int64_t ldt;
     int64_t ldz;
     int M, H, V;
-    int tiles;   // vocab tiles: ceil(V / 16) for the small-row kernel, ceil(V / 32) for the batched one
+    int tiles;   // vocab tiles: ceil(V / 32)
     int G;       // workgroups along the vocabulary
 };
 
@@ -67,194 +56,10 @@ __device__ __forceinline__ void static_for_impl(F&& f) {
 template <int N, class F>
 __device__ __forceinline__ void static_for(F&& f) { static_for_impl<0, N>(f); }
 
-constexpr int gcd_c(int x, int y) { return y == 0 ? x : gcd_c(y, x % y); }
-constexpr int lcm3(int x, int y, int z) {
-    return (x / gcd_c(x, y) * y) / gcd_c(x / gcd_c(x, y) * y, z) * z;
-}
-
-template <int MT, int NT, int DEPTH>
-__global__ void __launch_bounds__(kThreads) lmhead_gemm_lse_kernel(LmHeadArgs a) {
-    constexpr int ROWS = MT * 16;
-    constexpr int CHUNKS = ROWS * (kBK / 8);                  // 16-byte pieces of a hidden stage
-    constexpr int PER_THREAD = (CHUNKS + kThreads - 1) / kThreads;
-    // one spare row takes the writes of the surplus threads of the last hidden
-    // chunk round, so that stores need no branch
-    __shared__ __attribute__((aligned(16))) uint8_t hs[2][ROWS + 1][kRowBytes];
-    __shared__ float2 wpart[4][ROWS];
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int b = blockIdx.x;
-    const int m0 = blockIdx.y * ROWS;
-    const int t_begin = (int)((int64_t)b * a.tiles / a.G);
-    const int t_end = (int)((int64_t)(b + 1) * a.tiles / a.G);
-    const int H = a.H;
-    const int nks = (H + kBK - 1) / kBK;
-    const int lr = lane & 15, lg = lane >> 4;
-
-    float run_m = 0.f, run_s = 0.f;   // running LSE partial of row m0 + tid (s == 0: empty)
-
-    // hidden stage ks -> registers.  Loads are never skipped or masked at load
-    // time: an out-of-range piece loads a clamped, valid address and is zeroed
-    // when it is written to LDS.  (A branch or a select right after a load makes
-    // the compiler wait for that load at once, which would serialise the pipeline.)
-    auto load_h = [&](int ks, bf16x8 (&reg)[PER_THREAD]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < PER_THREAD; ++i) {
-            const int c = tid + i * kThreads;
-            const int row = c >> 3, col = ks * kBK + (c & 7) * 8;
-            const int grow = min(m0 + row, a.M - 1), gcol = min(col, H - 8);
-            reg[i] = *reinterpret_cast<const bf16x8*>(a.hidden + (int64_t)grow * H + gcol);
-        }
-    };
-    auto store_h = [&](int buf, int ks, const bf16x8 (&reg)[PER_THREAD]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < PER_THREAD; ++i) {
-            const int c = tid + i * kThreads;
-            const int row = c >> 3, col = ks * kBK + (c & 7) * 8;
-            const bool ok = c < CHUNKS && m0 + row < a.M && col < H;
-            *reinterpret_cast<bf16x8*>(&hs[buf][min(row, ROWS)][(c & 7) * 16]) = ok ? reg[i] : bf16x8{};
-        }
-    };
-
-    for (int pt = t_begin; pt < t_end; pt += 4 * NT) {
-        const int npass = min(4 * NT, t_end - pt);
-        const bf16x8* wrow[NT];
-        bool tvalid[NT];
-#pragma unroll
-        for (int j = 0; j < NT; ++j) {
-            const int tloc = wave + 4 * j;
-            tvalid[j] = tloc < npass;
-            int v = (pt + tloc) * 16 + lr;
-            v = min(v, a.V - 1);   // rows past the vocabulary load a valid row; their results are dropped
-            wrow[j] = reinterpret_cast<const bf16x8*>(a.W + (int64_t)v * H);
-        }
-        auto load_w = [&](int ks, bf16x8 (&w)[NT][2]) __attribute__((always_inline)) {
-#pragma unroll
-            for (int j = 0; j < NT; ++j) {
-#pragma unroll
-                for (int s = 0; s < 2; ++s) {
-                    const int col = ks * kBK + lg * 16 + s * 8;
-                    // columns past H meet zeroed hidden values; rows of invalid tiles are dropped
-                    w[j][s] = __builtin_nontemporal_load(wrow[j] + (min(col, H - 8) >> 3));
-                }
-            }
-        };
-
-        f32x4 acc[MT][NT];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int j = 0; j < NT; ++j) acc[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-        // Software pipeline over 64-wide h steps.  W(s) is loaded at step s-(DEPTH-1) into
-        // wbuf[s % DEPTH]; hidden(s) is loaded at step s-2 into hreg[s % 2] and written to
-        // LDS buffer s % 2 at the end of step s-1.  Every W load is issued after the hidden
-        // load that the next LDS write waits for, so that wait never forces a young W load.
-        bf16x8 hreg[2][PER_THREAD];
-        bf16x8 wbuf[DEPTH][NT][2];
-        load_h(0, hreg[0]);
-        load_h(1, hreg[1]);
-#pragma unroll
-        for (int d = 0; d < DEPTH - 1; ++d) load_w(d, wbuf[d]);
-        store_h(0, 0, hreg[0]);
-        __syncthreads();
-
-        // one 64-wide step: prefetch hidden(ks+2) and W(ks+DEPTH-1), multiply step ks,
-        // write hidden(ks+1) to LDS.  In the main loop nothing is conditional
-        // (prefetches past the end read clamped addresses and are never used), so
-        // the compiler can count outstanding loads exactly.
-        auto step = [&](auto U, int ks) __attribute__((always_inline)) {
-            constexpr int u = decltype(U)::value;
-            load_h(ks + 2, hreg[u & 1]);
-            load_w(ks + DEPTH - 1, wbuf[(u + DEPTH - 1) % DEPTH]);
-            // the B fragments of row tile mt+1 are read from LDS while tile mt multiplies
-            const uint8_t* base = &hs[u & 1][lr][lg * 32];
-            bf16x8 hb[2][2];
-            hb[0][0] = *reinterpret_cast<const bf16x8*>(base);
-            hb[0][1] = *reinterpret_cast<const bf16x8*>(base + 16);
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                if (mt + 1 < MT) {
-                    const uint8_t* rowp = base + (mt + 1) * 16 * kRowBytes;
-                    hb[(mt + 1) & 1][0] = *reinterpret_cast<const bf16x8*>(rowp);
-                    hb[(mt + 1) & 1][1] = *reinterpret_cast<const bf16x8*>(rowp + 16);
-                }
-#pragma unroll
-                for (int j = 0; j < NT; ++j)
-                    acc[mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wbuf[u % DEPTH][j][0], hb[mt & 1][0], acc[mt][j], 0, 0, 0);
-#pragma unroll
-                for (int j = 0; j < NT; ++j)
-                    acc[mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wbuf[u % DEPTH][j][1], hb[mt & 1][1], acc[mt][j], 0, 0, 0);
-            }
-            store_h((u + 1) & 1, ks + 1, hreg[(u + 1) & 1]);
-            __syncthreads();
-        };
-        // UN steps per iteration keep every ring slot a compile-time register choice
-        constexpr int UN = (DEPTH % 2 == 0) ? DEPTH : 2 * DEPTH;
-        const int nmain = nks - nks % UN;
-        for (int ks0 = 0; ks0 < nmain; ks0 += UN) {
-            static_for<UN>([&](auto U) __attribute__((always_inline)) { step(U, ks0 + decltype(U)::value); });
-        }
-        // the remaining steps use the same slots, since nmain is a multiple of UN
-        static_for<UN - 1>([&](auto U) __attribute__((always_inline)) {
-            if (nmain + decltype(U)::value < nks) step(U, nmain + decltype(U)::value);
-        });
-
-        // ---- epilogue of the pass: store logits, fold the rows' (max, sum exp) partials
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const int m = m0 + mt * 16 + lr;
-            float mx = -INFINITY;
-#pragma unroll
-            for (int j = 0; j < NT; ++j) {
-                const int v0 = (pt + wave + 4 * j) * 16 + lg * 4;
-                const f32x4 z = acc[mt][j];
-                if (tvalid[j] && m < a.M) {
-                    float* dst = a.logits + (int64_t)m * a.ldz + v0;
-                    if (v0 + 3 < a.V) {
-                        *reinterpret_cast<f32x4*>(dst) = z;
-                    } else {
-#pragma unroll
-                        for (int q = 0; q < 4; ++q)
-                            if (v0 + q < a.V) dst[q] = z[q];
-                    }
-                }
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    if (tvalid[j] && v0 + q < a.V) mx = fmaxf(mx, z[q]);
-            }
-            float sm = 0.f;
-#pragma unroll
-            for (int j = 0; j < NT; ++j) {
-                const int v0 = (pt + wave + 4 * j) * 16 + lg * 4;
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    if (tvalid[j] && v0 + q < a.V) sm += __expf(acc[mt][j][q] - mx);
-            }
-            // the four lanes lr, lr+16, lr+32, lr+48 hold the same row
-#pragma unroll
-            for (int o = 16; o <= 32; o <<= 1) {
-                const float m2 = __shfl_xor(mx, o);
-                const float s2 = __shfl_xor(sm, o);
-                lse_merge(mx, sm, m2, s2);
-            }
-            if (lg == 0) wpart[wave][mt * 16 + lr] = make_float2(mx, sm);
-        }
-        __syncthreads();
-        if (tid < ROWS) {
-#pragma unroll
-            for (int w = 0; w < 4; ++w) lse_merge(run_m, run_s, wpart[w][tid].x, wpart[w][tid].y);
-        }
-        __syncthreads();
-    }
-    if (tid < ROWS && m0 + tid < a.M)
-        a.part[(int64_t)(m0 + tid) * a.G + b] = make_float2(run_m, run_s);
-}
-
-// ---------------------------------------------------------------- batched rows (more than 64)
+// ---------------------------------------------------------------- the kernel
 // Four waves, one per SIMD, so that each wave may hold up to 512 registers:
-// wave w accumulates NV = 2 vocab tiles of 32 rows for all MT 32-row batch
-// tiles of its row chunk (2 MT 32x32 fp32 accumulators, in AGPRs), using
+// wave w accumulates NV (1 or 2) vocab tiles of 32 rows for all MT 32-row batch
+// tiles of its row chunk (NV MT 32x32 fp32 accumulators, in AGPRs), using
 // v_mfma_f32_32x32x16_bf16 (on gfx950 it sustains about 2.2 PFLOP/s with two
 // accumulator chains; the 16x16x32 form reaches barely half).
 //
@@ -316,13 +121,13 @@ __device__ __forceinline__ void dma16(u32x4 rsrc, uint32_t lds, int voff, int so
                  : "memory", "m0");
 }
 
-constexpr int kNV = 2;                    // vocab tiles per wave and pass
+constexpr int kNV = 2;                    // vocab tiles per wave and pass (more than 64 rows)
 constexpr int kWSlots = 3;                // W slots per wave: W runs kWSlots - 1 steps ahead
-template <int MT, bool HFULL, int SW = kWSlots>
+template <int MT, bool HFULL, int NVT, int SW = kWSlots>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 lmhead_dma_kernel(LmHeadArgs a) {
     static_assert(SW >= 3, "the wait before each barrier assumes W is issued two or more steps ahead");
-    constexpr int NV = kNV;
+    constexpr int NV = NVT;
     constexpr int WJ = NV * 4;                   // W DMA instructions per wave and step
     constexpr int HR = MT * 32;                  // batch rows staged
     constexpr int WR = NV * 32;                  // W rows of one wave per pass
@@ -575,44 +380,29 @@ lmhead_dma_kernel(LmHeadArgs a) {
     }
 }
 
-template <int MT>
-hipError_t launch_mt(const LmHeadArgs& a, dim3 grid, hipStream_t s) {
-    hipLaunchKernelGGL((lmhead_gemm_lse_kernel<MT, kNT, kDepth>), grid, dim3(kThreads), 0, s, a);
-    return hipGetLastError();
-}
-
-template <int MT>
+template <int MT, int NV>
 hipError_t launch_rows(const LmHeadArgs& a, dim3 grid, hipStream_t s) {
     if (a.H % kBK == 0)
-        hipLaunchKernelGGL((lmhead_dma_kernel<MT, true>), grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((lmhead_dma_kernel<MT, true, NV>), grid, dim3(256), 0, s, a);
     else
-        hipLaunchKernelGGL((lmhead_dma_kernel<MT, false>), grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((lmhead_dma_kernel<MT, false, NV>), grid, dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
-// Up to 64 rows: the vocab-split kernel with ceil(M / 16) row tiles.  More:
-// the batched kernel on row chunks of up to 256 rows (eight 32-row tiles: 256
-// AGPRs of accumulators and all 160 KB of LDS).
+// Row chunks of up to 256 rows (eight 32-row tiles: 256 AGPRs of accumulators
+// and all 160 KB of LDS); up to 64 rows one vocab tile per wave and pass.
 constexpr int kMaxChunkRows = 256;
-constexpr int kRowsTilesPerPass = 4 * kNV;
-bool small_rows(int M) { return M <= 64; }
-int row_tiles_small(int M) { return M <= 0 ? 1 : (M + 15) / 16; }
-int row_chunks(int M) { return (M + kMaxChunkRows - 1) / kMaxChunkRows; }
+int vocab_tiles_per_wave(int M) { return M <= 64 ? 1 : kNV; }
+int row_chunks(int M) { return M <= kMaxChunkRows ? 1 : (M + kMaxChunkRows - 1) / kMaxChunkRows; }
 int chunk_tiles(int M) {   // 32-row tiles per chunk
     const int gy = row_chunks(M);
     return ((M + gy - 1) / gy + 31) / 32;
 }
-// workgroups along the vocabulary
+// workgroups along the vocabulary: one per CU (256 on MI355X) over all row chunks
 int lmhead_grid(int M, int V) {
-    if (small_rows(M)) {
-        const int tiles = (V + 15) / 16;
-        const int need = (tiles + 4 * kNT - 1) / (4 * kNT);
-        const int cap = row_tiles_small(M) <= 2 ? 1024 : 512;
-        return need < cap ? need : cap;
-    }
-    // one workgroup per CU (256 on MI355X) over all row chunks
     const int tiles = (V + 31) / 32;
-    const int need = (tiles + kRowsTilesPerPass - 1) / kRowsTilesPerPass;
+    const int per_pass = 4 * vocab_tiles_per_wave(M);
+    const int need = (tiles + per_pass - 1) / per_pass;
     const int cap = 256 / row_chunks(M) > 0 ? 256 / row_chunks(M) : 1;
     return need < cap ? need : cap;
 }
@@ -650,39 +440,29 @@ __global__ void __launch_bounds__(256) row_lse_kernel(const float* logits, int64
 
 }  // namespace
 
-int lmhead_partials(int M, int V) {
-    return small_rows(M) ? lmhead_grid(M, V) : lmhead_grid(M, V) * kRowsWaves;
-}
+int lmhead_partials(int M, int V) { return lmhead_grid(M, V) * kRowsWaves; }
 
-bool lmhead_has_tile_max(int M) { return !small_rows(M); }
+bool lmhead_has_tile_max(int M) { return M > 0; }
 
 hipError_t launch_lmhead(const uint16_t* hidden, const uint16_t* W, float* logits, int64_t ldz,
                          float2* lse_part, float* tile_max, int64_t ldt, int M, int H, int V, hipStream_t s) {
     if (M <= 0) return hipSuccess;
     LmHeadArgs a;
     a.hidden = hidden; a.W = W; a.logits = logits; a.part = lse_part; a.ldz = ldz;
-    a.tmax = small_rows(M) ? nullptr : tile_max; a.ldt = ldt;
+    a.tmax = tile_max; a.ldt = ldt;
     a.M = M; a.H = H; a.V = V;
     a.G = lmhead_grid(M, V);
-    if (small_rows(M)) {
-        a.tiles = (V + 15) / 16;
-        const dim3 grid(a.G, 1);
-        switch (row_tiles_small(M)) {
-            case 1: return launch_mt<1>(a, grid, s);
-            case 2: return launch_mt<2>(a, grid, s);
-            case 3: return launch_mt<3>(a, grid, s);
-            default: return launch_mt<4>(a, grid, s);
-        }
-    }
     a.tiles = (V + 31) / 32;
     const dim3 grid(a.G, row_chunks(M));
     switch (chunk_tiles(M)) {
-        case 3: return launch_rows<3>(a, grid, s);
-        case 4: return launch_rows<4>(a, grid, s);
-        case 5: return launch_rows<5>(a, grid, s);
-        case 6: return launch_rows<6>(a, grid, s);
-        case 7: return launch_rows<7>(a, grid, s);
-        default: return launch_rows<8>(a, grid, s);
+        case 1: return launch_rows<1, 1>(a, grid, s);
+        case 2: return launch_rows<2, 1>(a, grid, s);
+        case 3: return launch_rows<3, kNV>(a, grid, s);
+        case 4: return launch_rows<4, kNV>(a, grid, s);
+        case 5: return launch_rows<5, kNV>(a, grid, s);
+        case 6: return launch_rows<6, kNV>(a, grid, s);
+        case 7: return launch_rows<7, kNV>(a, grid, s);
+        default: return launch_rows<8, kNV>(a, grid, s);
     }
 }
 
