@@ -10,9 +10,9 @@
 //   g_p = sigmoid(w . h_p) when gated, else 1.
 // One workgroup per (position, request).  The K rows of A and of B it needs
 // are gathered whole (up to 256 rank elements at a time), every load in flight
-// at once, into LDS rows of 260 floats; thread (tj, tk) accumulates S[tj +
-// 16 x][tk + 16 y] for x, y < 4 in a fixed order over the rank (ascending), so
-// that its float4 reads of 16 consecutive B rows fall in distinct LDS banks.
+// at once, into LDS rows of 260 floats (the 32 rows a wave reads fall in
+// distinct banks); each of the four waves computes one 32 x 32 quadrant of S
+// with fp32 MFMAs.
 //
 // Walk (same commit: the greedy walk takes the best candidate after the token
 // before; the max-score walk is its Viterbi form): one 256-thread workgroup per
@@ -98,12 +98,14 @@ __global__ void __launch_bounds__(kPairThreads) pair_scores_kernel(
 
     const float* TA = tables;
     const float* TB = tables + (int64_t)Vt * r;
-    const int tj = tid >> 4, tk = tid & 15;
-    float acc[4][4];
-#pragma unroll
-    for (int x = 0; x < 4; ++x)
-#pragma unroll
-        for (int y = 0; y < 4; ++y) acc[x][y] = 0.f;
+    // wave w computes the 32 x 32 quadrant (jt, kt) = (w / 2, w % 2) of S on the matrix
+    // cores (v_mfma_f32_32x32x2_f32, fp32 products and sums): in MFMA step s lane l
+    // supplies A[prev 32 jt + l % 32][k] and B[cand 32 kt + l % 32][k] with k = 8 (s / 4)
+    // + 4 (l / 32) + s % 4, the same in both, read as float4 from the LDS rows
+    const int lane = tid & 63, wv = tid >> 6;
+    const int lr = lane & 31, lh = lane >> 5;
+    const int jt = wv >> 1, kt = wv & 1;
+    f32x16 acc = f32x16{};
 
     // With r % 4 == 0 and 16-byte aligned tables every row is read as float4:
     // float4 f of a slice is row f / 64 (A rows, then B rows), elements 4 (f % 64) ..
@@ -135,33 +137,25 @@ __global__ void __launch_bounds__(kPairThreads) pair_scores_kernel(
             }
         }
         __syncthreads();
-        const int w4 = (w + 3) >> 2;                  // elements past w are zero in both operands
-        for (int i4 = 0; i4 < w4; ++i4) {
-            f32x4 av[4], bv[4];
+        const int w8 = (w + 7) >> 3;                  // elements past w are zero in both operands
+        const float* arow = &As[32 * jt + lr][4 * lh];
+        const float* brow = &Bs[32 * kt + lr][4 * lh];
+        for (int gi = 0; gi < w8; ++gi) {
+            const f32x4 av = *reinterpret_cast<const f32x4*>(arow + 8 * gi);
+            const f32x4 bv = *reinterpret_cast<const f32x4*>(brow + 8 * gi);
 #pragma unroll
-            for (int x = 0; x < 4; ++x) av[x] = *reinterpret_cast<const f32x4*>(&As[tj + 16 * x][4 * i4]);
-#pragma unroll
-            for (int y = 0; y < 4; ++y) bv[y] = *reinterpret_cast<const f32x4*>(&Bs[tk + 16 * y][4 * i4]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-#pragma unroll
-                for (int x = 0; x < 4; ++x)
-#pragma unroll
-                    for (int y = 0; y < 4; ++y) acc[x][y] = fmaf(av[x][e], bv[y][e], acc[x][y]);
+            for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av[e], bv[e], acc, 0, 0, 0);
         }
         __syncthreads();
     }
 
+    // register i of lane l: S[32 jt + 8 (i / 4) + 4 (l / 32) + i % 4][32 kt + l % 32]
     float* out = pair + (int64_t)m * K * K;
+    const int k = 32 * kt + lr;
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
-        const int j = tj + 16 * x;
-        if (j >= K) continue;
-#pragma unroll
-        for (int y = 0; y < 4; ++y) {
-            const int k = tk + 16 * y;
-            if (k < K) out[(int64_t)j * K + k] = (j < Jn) ? g * acc[x][y] : 0.f;
-        }
+    for (int i = 0; i < 16; ++i) {
+        const int j = 32 * jt + 8 * (i / 4) + 4 * lh + i % 4;
+        if (j < K && k < K) out[(int64_t)j * K + k] = (j < Jn) ? g * acc[i] : 0.f;
     }
 }
 
