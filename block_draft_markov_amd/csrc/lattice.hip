@@ -246,11 +246,19 @@ __global__ void __launch_bounds__(kWalkThreads) walk_kernel(const int64_t* __res
                 } else {
                     float best = -INFINITY;
                     int arg = 16 * q;
-                    const int j0 = 16 * q, j1 = min(16 * q + 16, K);
-                    for (int j = j0; j < j1; ++j) {
-                        const float dj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(d), j));
-                        const float v = dj + Ss[buf][pp][j * 64 + lane];
-                        if (v > best) { best = v; arg = j; }
+                    // the 16 S entries of this quarter first (their LDS reads overlap), then
+                    // the max in ascending j with strict >, so the lowest j wins a tie
+                    float sv[16];
+#pragma unroll
+                    for (int t = 0; t < 16; ++t) sv[t] = Ss[buf][pp][(16 * q + t) * 64 + lane];
+#pragma unroll
+                    for (int t = 0; t < 16; ++t) {
+                        const int j = 16 * q + t;
+                        if (j < K) {
+                            const float dj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(d), j));
+                            const float v = dj + sv[t];
+                            if (v > best) { best = v; arg = j; }
+                        }
                     }
                     qbest[par][q][lane] = best;
                     qarg[par][q][lane] = arg;
