@@ -377,17 +377,18 @@ __global__ void __launch_bounds__(kThreads) topk_tiles_kernel(const float* __res
     const int nsel = s_nsel;
     bool exact = nsel > kSelCap;
     if (!exact) {
-        // ---- their logits >= tau (eight loads in flight per thread at a time)
-        for (int base = 0; base < nsel * 32; base += kThreads * 8) {
-            float zv[8];
+        // ---- their logits >= tau (sixteen loads in flight per thread at a time: one round
+        // for up to 128 tiles)
+        for (int base = 0; base < nsel * 32; base += kThreads * 16) {
+            float zv[16];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
+            for (int i = 0; i < 16; ++i) {
                 const int e = base + tid + kThreads * i;
                 const int v = e < nsel * 32 ? sel[e >> 5] * 32 + (e & 31) : V;
                 zv[i] = v < V ? row[v] : 0.f;
             }
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
+            for (int i = 0; i < 16; ++i) {
                 const int e = base + tid + kThreads * i;
                 const int v = e < nsel * 32 ? sel[e >> 5] * 32 + (e & 31) : V;
                 if (v < V) {
