@@ -154,6 +154,12 @@ lmhead_dma_kernel(LmHeadArgs a) {
     const int npass = nfull + (rest > 0);
     const int nv_last = rest <= 4 ? 1 : NV;
     const int split = nv_last == 1 && rest > 0 ? nfull : npass;   // passes before the one-tile pass
+    // Odd workgroups run their one-tile pass first, so that the logits stores at the
+    // ends of passes are not issued by every CU at the same moment.
+    const bool short_first = (b & 1) && split < npass;
+    auto stream_pass = [&](int q) __attribute__((always_inline)) {   // logical pass of stream position q
+        return short_first ? (q == 0 ? split : q - 1) : q;
+    };
     auto pass_first = [&](int p) __attribute__((always_inline)) {
         const int nv = p < nfull ? NV : nv_last;
         return t_begin + p * 4 * NV + wave * nv;
@@ -173,8 +179,9 @@ lmhead_dma_kernel(LmHeadArgs a) {
     int wvoff[WJ];
     int wp = 0, wks = 0;                         // W DMA cursor (pass, step); wp == npass: past the end
     auto set_w = [&](int p) __attribute__((always_inline)) {
-        const int cnt = p < npass ? pass_count(p) : 0;
-        const int base = min(pass_first(p < npass ? p : npass - 1), a.tiles - 1) * 32;
+        const int lp = stream_pass(p < npass ? p : npass - 1);
+        const int cnt = p < npass ? pass_count(lp) : 0;
+        const int base = min(pass_first(lp), a.tiles - 1) * 32;
         const int64_t rest_bytes = (int64_t)(a.V - base) * H * 2;
         const int64_t span = (int64_t)WR * H * 2;
         wbuf = sbuf(a.W + (int64_t)base * H, rest_bytes < span ? rest_bytes : span);
@@ -235,9 +242,9 @@ lmhead_dma_kernel(LmHeadArgs a) {
 #pragma unroll
         for (int s = 0; s < 4; ++s) foff[par][s] = lr * 128 + (((4 * lh + s) ^ swz(lr) ^ (4 * par)) * 16);
 
-    float run_m[MT], run_s[MT];
+    float run_m[MT], run_s[MT];     // running (max, sum exp) of the lane's half of its rows
 #pragma unroll
-    for (int i = 0; i < MT; ++i) { run_m[i] = 0.f; run_s[i] = 0.f; }
+    for (int i = 0; i < MT; ++i) { run_m[i] = -INFINITY; run_s[i] = 0.f; }
 
     // ---- MFMAs of one step for NA tiles: W fragments first, then batch tiles, reads one tile ahead
     auto mfma_step = [&](auto& acc, uint32_t hs, uint32_t ws) __attribute__((always_inline)) {
@@ -272,14 +279,21 @@ lmhead_dma_kernel(LmHeadArgs a) {
         });
     };
 
-    // ---- pass epilogue: logits of the wave's tiles and their (max, sum exp) per batch row
+    // ---- pass epilogue: logits of the wave's tiles, the tile maxima and the running
+    // (max, sum exp) of the batch rows.  Each lane keeps its own running pair for the 16
+    // logits of a row it holds (online: the sum is rescaled when the maximum grows), and
+    // the two lanes of a row are merged once at the end; a whole tile inside the
+    // vocabulary takes a branch-free path.
     auto epilogue = [&](auto& acc, int p) __attribute__((always_inline)) {
         constexpr int NA = std::extent<std::remove_reference_t<decltype(acc)>>::value;
+        constexpr float kL2E = 1.4426950408889634f;
         const int f = pass_first(p), cnt = pass_count(p);
 #pragma unroll
         for (int v = 0; v < NA; ++v) {
             if (v < cnt) {
                 const int tile = f + v;
+                const int col = tile * 32 + 4 * lh;          // first logit of the lane, then +8 g + q
+                const bool full = (tile + 1) * 32 <= a.V;
 #pragma unroll
                 for (int i = 0; i < MT; ++i) {
                     const int m = m0 + i * 32 + lr;
@@ -291,38 +305,47 @@ lmhead_dma_kernel(LmHeadArgs a) {
                         asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(x) : "a"(acc[v][i][j]));
                         z[j] = x;
                     }
-                    float mx = -INFINITY;
+                    if (!full) {
 #pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const int v0 = tile * 32 + 8 * g + 4 * lh;
-                        const f32x4 z4 = {z[4 * g], z[4 * g + 1], z[4 * g + 2], z[4 * g + 3]};
-                        if (m < a.M) {
-                            float* dst = a.logits + (int64_t)m * a.ldz + v0;
-                            if (v0 + 3 < a.V) {
-                                *reinterpret_cast<f32x4*>(dst) = z4;
-                            } else {
+                        for (int j = 0; j < 16; ++j)
+                            if (col + 8 * (j >> 2) + (j & 3) >= a.V) z[j] = -INFINITY;
+                    }
+                    if (m < a.M) {
+                        float* dst = a.logits + (int64_t)m * a.ldz + col;
+                        if (full) {
 #pragma unroll
-                                for (int q = 0; q < 4; ++q)
-                                    if (v0 + q < a.V) dst[q] = z4[q];
-                            }
+                            for (int g = 0; g < 4; ++g)
+                                *reinterpret_cast<f32x4*>(dst + 8 * g) =
+                                    f32x4{z[4 * g], z[4 * g + 1], z[4 * g + 2], z[4 * g + 3]};
+                        } else {
+#pragma unroll
+                            for (int j = 0; j < 16; ++j)
+                                if (col + 8 * (j >> 2) + (j & 3) < a.V) dst[8 * (j >> 2) + (j & 3)] = z[j];
                         }
-#pragma unroll
-                        for (int q = 0; q < 4; ++q)
-                            if (v0 + q < a.V) mx = fmaxf(mx, z4[q]);
                     }
-                    float sm = 0.f;
-#pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const int v0 = tile * 32 + 8 * g + 4 * lh;
-#pragma unroll
-                        for (int q = 0; q < 4; ++q)
-                            if (v0 + q < a.V) sm += __expf(z[4 * g + q] - mx);
+                    float mx = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])),
+                                     fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
+                    mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(z[8], z[9]), fmaxf(z[10], z[11])),
+                                         fmaxf(fmaxf(z[12], z[13]), fmaxf(z[14], z[15]))));
+                    if (a.tmax) {
+                        // lanes l and l ^ 32 hold the two halves of the row's tile
+                        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                                          false, false);
+                        const float tm = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+                        if (lh == 0 && m < a.M) a.tmax[(int64_t)m * a.ldt + tile] = tm;
                     }
-                    const float m2 = __shfl_xor(mx, 32);
-                    const float s2 = __shfl_xor(sm, 32);
-                    if (a.tmax && lh == 0 && m < a.M) a.tmax[(int64_t)m * a.ldt + tile] = fmaxf(mx, m2);
-                    lse_merge(mx, sm, m2, s2);
-                    lse_merge(run_m[i], run_s[i], mx, sm);
+                    const float nm = fmaxf(run_m[i], mx);
+                    if (full || nm != -INFINITY) {
+                        const float nml = nm * kL2E;
+                        float s0 = run_s[i] * __builtin_amdgcn_exp2f(run_m[i] * kL2E - nml), s1 = 0.f;
+#pragma unroll
+                        for (int j = 0; j < 16; j += 2) {
+                            s0 += __builtin_amdgcn_exp2f(__builtin_fmaf(z[j], kL2E, -nml));
+                            s1 += __builtin_amdgcn_exp2f(__builtin_fmaf(z[j + 1], kL2E, -nml));
+                        }
+                        run_s[i] = s0 + s1;
+                        run_m[i] = nm;
+                    }
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
@@ -366,17 +389,24 @@ lmhead_dma_kernel(LmHeadArgs a) {
                 epilogue(acc, p);
             }
         };
-        run(std::integral_constant<int, NV>{}, 0, split);
-        if (split < npass) run(std::integral_constant<int, 1>{}, split, npass);
+        if (short_first) {
+            run(std::integral_constant<int, 1>{}, split, npass);
+            run(std::integral_constant<int, NV>{}, 0, split);
+        } else {
+            run(std::integral_constant<int, NV>{}, 0, split);
+            if (split < npass) run(std::integral_constant<int, 1>{}, split, npass);
+        }
         // the loads issued past the last step write LDS: let them land before the workgroup ends
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     }
-    if (lh == 0) {
 #pragma unroll
-        for (int i = 0; i < MT; ++i) {
-            const int m = m0 + i * 32 + lr;
-            if (m < a.M) a.part[(int64_t)m * a.G * kRowsWaves + b * kRowsWaves + wave] = make_float2(run_m[i], run_s[i]);
-        }
+    for (int i = 0; i < MT; ++i) {
+        // merge the two halves of each row (an empty half has s = 0)
+        float rm = run_m[i], rs = run_s[i];
+        lse_merge(rm, rs, __shfl_xor(rm, 32), __shfl_xor(rs, 32));
+        const int m = m0 + i * 32 + lr;
+        if (lh == 0 && m < a.M)
+            a.part[(int64_t)m * a.G * kRowsWaves + b * kRowsWaves + wave] = make_float2(rm, rs);
     }
 }
 
