@@ -70,8 +70,7 @@ int check_dims(const dflash_dims* d) {
         return fail(DFLASH_EINVAL, "rank = %d outside [1, %lld]", d->rank, (long long)kMaxRank);
     if (d->walk != DFLASH_WALK_VITERBI && d->walk != DFLASH_WALK_GREEDY)
         return fail(DFLASH_EINVAL, "walk = %d is neither DFLASH_WALK_VITERBI nor DFLASH_WALK_GREEDY", d->walk);
-    const dflash::TopkPlan p = dflash::topk_plan(d->total_rows, d->draft_vocab, d->top_k);
-    if ((int64_t)p.nchunks * d->top_k > 2048)
+    if ((int64_t)dflash::topk_tiles_chunks(d->draft_vocab) * d->top_k > 2048)
         return fail(DFLASH_EUNSUPPORTED, "draft_vocab = %d is too large for top_k = %d", d->draft_vocab, d->top_k);
     return DFLASH_OK;
 }
@@ -93,7 +92,7 @@ int need(const void* p, int64_t count, const char* name) {
 struct Layout {
     int64_t ldz;
     int64_t ldt;      // tile maxima stride (0: none, the Top-K reads every logit)
-    size_t logits, lse, part, tmax, best, cidx, ctok, unary, pair, dense, total;
+    size_t logits, lse, part, tmax, cidx, ctok, unary, pair, dense, total;
     int nparts;
 };
 
@@ -102,7 +101,6 @@ Layout layout(const dflash_dims* d) {
     const int64_t M = d->total_rows, K = d->top_k;
     l.ldz = round_up(d->draft_vocab, 4);
     l.nparts = dflash::lmhead_partials(d->total_rows, d->draft_vocab);
-    const dflash::TopkPlan p = dflash::topk_plan(d->total_rows, d->draft_vocab, d->top_k);
     size_t off = 0;
     auto take = [&](size_t bytes) {
         const size_t at = off;
@@ -114,7 +112,6 @@ Layout layout(const dflash_dims* d) {
     l.part = take((size_t)(M * l.nparts) * sizeof(float2));
     l.ldt = dflash::lmhead_has_tile_max(d->total_rows) ? (d->draft_vocab + 31) / 32 : 0;
     l.tmax = take((size_t)(M * l.ldt) * sizeof(float));
-    l.best = take((size_t)(M * p.nchunks * K) * sizeof(uint64_t));
     l.cidx = take((size_t)(M * K) * sizeof(int32_t));
     l.ctok = take((size_t)(M * K) * sizeof(int64_t));
     l.unary = take((size_t)(M * K) * sizeof(float));
@@ -168,15 +165,11 @@ int lattice_stages(const dflash_dims* d, const uint16_t* hidden, const uint16_t*
     if ((e = dflash::launch_lmhead(hidden, lm_head, logits, l.ldz, part, tmax, l.ldt, d->total_rows, d->hidden,
                                    d->draft_vocab, s)) != hipSuccess)
         return hip_fail(e, "lm_head launch");
-    if (tmax)
-        e = dflash::launch_topk_tiles(logits, l.ldz, tmax, l.ldt, part, l.nparts, d2t, d->total_rows,
-                                      d->draft_vocab, d->top_k, at<int32_t>(ws, l.cidx), at<int64_t>(ws, l.ctok),
-                                      at<float>(ws, l.unary), s);
-    else
-        e = dflash::launch_topk(logits, l.ldz, nullptr, part, l.nparts, d2t, d->total_rows, d->draft_vocab,
-                                d->top_k, at<uint64_t>(ws, l.best), at<int32_t>(ws, l.cidx),
-                                at<int64_t>(ws, l.ctok), at<float>(ws, l.unary), s);
-    if (e != hipSuccess) return hip_fail(e, "top-k launch");
+    // the lm_head kernel stored the tile maxima (there are some whenever there are rows)
+    if ((e = dflash::launch_topk_tiles(logits, l.ldz, tmax, l.ldt, nullptr, part, l.nparts, d2t, d->total_rows,
+                                       d->draft_vocab, d->top_k, at<int32_t>(ws, l.cidx), at<int64_t>(ws, l.ctok),
+                                       at<float>(ws, l.unary), s)) != hipSuccess)
+        return hip_fail(e, "top-k launch");
     if ((e = dflash::launch_pair_scores(at<int64_t>(ws, l.ctok), tables, gate_w, hidden, last_tok, row_offsets,
                                         d->num_requests, d->block_len, d->total_rows, d->hidden, d->target_vocab,
                                         d->top_k, d->rank, at<float>(ws, l.pair), s)) != hipSuccess)
@@ -360,10 +353,14 @@ int dflash_topk(const dflash_dims* d, const float* logits, int64_t ldz, const fl
                     d->draft_vocab);
     Layout l;
     if ((rc = check_ws(d, ws, ws_bytes, l))) return rc;
-    hipError_t e = dflash::launch_topk(logits, ldz, lse, nullptr, 0, d2t, d->total_rows, d->draft_vocab, d->top_k,
-                                       at<uint64_t>(ws, l.best), cand_idx, cand_tok, unary,
-                                       static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return hip_fail(e, "top-k launch");
+    // one streaming pass for the tile maxima, then the Top-K reads only the tiles they keep
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    float* tmax = at<float>(ws, l.tmax);
+    hipError_t e = dflash::launch_tile_max(logits, ldz, d->total_rows, d->draft_vocab, tmax, l.ldt, s);
+    if (e != hipSuccess) return hip_fail(e, "tile-maxima launch");
+    if ((e = dflash::launch_topk_tiles(logits, ldz, tmax, l.ldt, lse, nullptr, 0, d2t, d->total_rows,
+                                       d->draft_vocab, d->top_k, cand_idx, cand_tok, unary, s)) != hipSuccess)
+        return hip_fail(e, "top-k launch");
     return ok();
 }
 

@@ -22,20 +22,18 @@ hipError_t launch_lse_combine(const float2* lse_part, int nparts, float* lse, in
 hipError_t launch_row_lse(const float* logits, int64_t ldz, float* lse, int M, int V, hipStream_t s);
 
 // ---------------------------------------------------------------- part 2: Top-K
-struct TopkPlan {
-    int per_thread;   // logits per thread in a chunk (16, 32 or 64)
-    int chunk;        // logits per chunk = 256 * per_thread
-    int nchunks;      // chunks per row
-};
-TopkPlan topk_plan(int M, int V, int K);
-hipError_t launch_topk(const float* logits, int64_t ldz, const float* lse, const float2* lse_part,
-                       int nparts, const int64_t* d2t, int M, int V, int K, uint64_t* chunk_best,
-                       int32_t* cand_idx, int64_t* cand_tok, float* unary, hipStream_t s);
-// Top-K from the tile maxima of the lm_head kernel (one workgroup per row; rows
-// with heavy ties take an exact path over all their logits in the same launch).
+// Chunks of 16384 logits per row on the exact path of the Top-K (rows with heavy
+// ties); that path merges nchunks * K entries in LDS.
+int topk_tiles_chunks(int V);
+// Top-K from the maxima of the 32-logit tiles (one workgroup per row; rows with
+// heavy ties take an exact path over all their logits in the same launch).  The lse
+// of a row is lse[m] when lse is given, else merged from its (max, sum exp) partials.
 hipError_t launch_topk_tiles(const float* logits, int64_t ldz, const float* tile_max, int64_t ldt,
-                             const float2* lse_part, int nparts, const int64_t* d2t, int M, int V, int K,
-                             int32_t* cand_idx, int64_t* cand_tok, float* unary, hipStream_t s);
+                             const float* lse, const float2* lse_part, int nparts, const int64_t* d2t, int M,
+                             int V, int K, int32_t* cand_idx, int64_t* cand_tok, float* unary, hipStream_t s);
+// tile_max [M][ldt]: the maximum of every 32-logit tile of every row of logits [M][ldz].
+hipError_t launch_tile_max(const float* logits, int64_t ldz, int M, int V, float* tile_max, int64_t ldt,
+                           hipStream_t s);
 
 // Head-less drafting: per row the lowest draft id maximizing the scaled, soft-capped
 // logit, from the tile maxima when given (ldt > 0), else from a scan of the row.

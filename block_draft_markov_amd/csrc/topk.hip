@@ -6,19 +6,20 @@
 // DFlash v2 and DSpark drafts ...", What does this PR do?; ties ordered by
 // index as in the TopP commit of the openvino.genai page).
 //
-// Stage 1 (topk_chunk): a grid of (chunk, row) workgroups; a chunk is 256
-// threads x PT logits held in registers, read from HBM once with 16-byte
-// loads.  Every logit becomes an order-preserving uint32 key.  If tau is the
-// K-th largest of the 256 per-thread maxima, at least K keys of the chunk are
-// >= tau, so every member of the chunk's top K is >= tau: only those
-// survivors (about K + 10 for smooth rows) are ranked, each by counting the
-// survivors that beat it, which yields the slot order directly.  When more
-// than 256 keys survive (heavy ties), an exact radix select on 8-bit digits
-// finds the K-th key instead, and equal keys are taken in id order.
-// Stage 2 (topk_merge): one workgroup per row merges the sorted per-chunk
-// lists pairwise in LDS (each entry's merged position = its own index + the
-// number of entries of the other list that beat it, by binary search), then
-// writes ids, target ids and unary scores.
+// The top K of a row is read from the maxima of its 32-logit tiles: if tau is
+// at most the K-th largest tile maximum, every member of the top K is >= tau and
+// sits in a tile whose maximum reaches tau, so only those tiles are read
+// (topk_tiles).  The lm_head kernel stores the tile maxima as it writes the
+// logits; for logits from elsewhere one streaming pass (tile_max) computes them.
+// Within a chunk of a row (the exact path for rows with heavy ties), tau is the
+// K-th largest of the 256 per-thread maxima: at least K keys of the chunk are
+// >= tau, and only those survivors (about K + 10 for smooth rows) are ranked,
+// each by counting the survivors that beat it, which yields the slot order
+// directly.  When more than 256 keys survive, an exact radix select on 8-bit
+// digits finds the K-th key instead, and equal keys are taken in id order.
+// Sorted per-chunk lists are merged pairwise in LDS (each entry's merged
+// position = its own index + the number of entries of the other list that beat
+// it, by binary search).
 // Entries are (key << 32 | ~id), so a larger entry is the better slot and
 // every comparison is one 64-bit compare.
 
@@ -210,16 +211,6 @@ __device__ __forceinline__ void chunk_select(const float* __restrict__ row, int 
     __syncthreads();
 }
 
-template <int PT>
-__global__ void __launch_bounds__(kThreads) topk_chunk_kernel(const float* __restrict__ logits, int64_t ldz,
-                                                              int V, int K, int nchunks,
-                                                              uint64_t* __restrict__ best) {
-    __shared__ ChunkShared sh;
-    const int c = blockIdx.x, m = blockIdx.y;
-    chunk_select<PT>(logits + (int64_t)m * ldz, c * (kThreads * PT), V, K,
-                     best + ((int64_t)m * nchunks + c) * K, sh);
-}
-
 // Number of entries of the descending list y[0..n) that are > x (strict) or
 // >= x (when `or_equal`).
 __device__ __forceinline__ int count_better(const uint64_t* y, int n, uint64_t x, bool or_equal) {
@@ -281,24 +272,6 @@ __device__ __forceinline__ void write_row(const uint64_t* list, int m, int K, in
     }
 }
 
-__global__ void __launch_bounds__(kThreads) topk_merge_kernel(const uint64_t* __restrict__ best, int nchunks, int K,
-                                                              const float* __restrict__ lse_in,
-                                                              const float2* __restrict__ lse_part, int nparts,
-                                                              const int64_t* __restrict__ d2t, int V,
-                                                              int32_t* __restrict__ cand_idx,
-                                                              int64_t* __restrict__ cand_tok,
-                                                              float* __restrict__ unary) {
-    extern __shared__ uint64_t lists[];   // 2 * nchunks * K entries
-    __shared__ float2 red[4];
-    const int m = blockIdx.x;
-    const uint64_t* src = best + (int64_t)m * nchunks * K;
-    for (int i = threadIdx.x; i < nchunks * K; i += kThreads) lists[i] = src[i];
-    const float lse = row_lse_value(m, lse_in, lse_part, nparts, red);
-    __syncthreads();
-    const uint64_t* fin = merge_lists(lists, lists + (int64_t)nchunks * K, nchunks, K);
-    write_row(fin, m, K, V, lse, d2t, cand_idx, cand_tok, unary);
-}
-
 // ---------------------------------------------------------------- from tile maxima
 // When the lm_head kernel also stored the maximum of every 32-logit tile of
 // every row, the top K of a row needs only a few of its tiles.  If tau is at
@@ -315,6 +288,7 @@ constexpr int kTileCap = 8192;   // tile-maxima keys kept in LDS (32 KB); longer
 __global__ void __launch_bounds__(kThreads) topk_tiles_kernel(const float* __restrict__ logits, int64_t ldz,
                                                               const float* __restrict__ tmax, int64_t ldt,
                                                               int tiles, int V, int K, int nchunks,
+                                                              const float* __restrict__ lse_in,
                                                               const float2* __restrict__ lse_part, int nparts,
                                                               const int64_t* __restrict__ d2t,
                                                               int32_t* __restrict__ cand_idx,
@@ -343,7 +317,7 @@ __global__ void __launch_bounds__(kThreads) topk_tiles_kernel(const float* __res
         const int t = tid + kThreads * i;
         tv[i] = t < tiles ? trow[t] : 0.f;
     }
-    const float lse = block_lse(lse_part, m, nparts, red);
+    const float lse = row_lse_value(m, lse_in, lse_part, nparts, red);
 
     // ---- tau from the tile maxima
     uint32_t mx = 0;
@@ -418,56 +392,7 @@ __global__ void __launch_bounds__(kThreads) topk_tiles_kernel(const float* __res
     write_row(fin, m, K, V, lse, d2t, cand_idx, cand_tok, unary);
 }
 
-template <int PT>
-hipError_t launch_chunks(const float* logits, int64_t ldz, int V, int K, int M, int nchunks, uint64_t* best,
-                         hipStream_t s) {
-    hipLaunchKernelGGL((topk_chunk_kernel<PT>), dim3(nchunks, M), dim3(kThreads), 0, s, logits, ldz, V, K,
-                       nchunks, best);
-    return hipGetLastError();
-}
-
 }  // namespace
-
-TopkPlan topk_plan(int M, int V, int K) {
-    // The largest chunk that still gives about four workgroups per CU, as long
-    // as the per-row merge holds at most 2048 entries (2 x 16 KB of LDS).
-    TopkPlan p{16, 256 * 16, 0};
-    const int pts[3] = {64, 32, 16};
-    for (int i = 0; i < 3; ++i) {
-        const int chunk = 256 * pts[i];
-        const int nc = (V + chunk - 1) / chunk;
-        if ((int64_t)M * nc >= 1024 || pts[i] == 16) {
-            p.per_thread = pts[i];
-            p.chunk = chunk;
-            p.nchunks = nc;
-            break;
-        }
-    }
-    while ((int64_t)p.nchunks * K > 2048 && p.per_thread < 64) {
-        p.per_thread *= 2;
-        p.chunk = 256 * p.per_thread;
-        p.nchunks = (V + p.chunk - 1) / p.chunk;
-    }
-    return p;
-}
-
-hipError_t launch_topk(const float* logits, int64_t ldz, const float* lse, const float2* lse_part, int nparts,
-                       const int64_t* d2t, int M, int V, int K, uint64_t* chunk_best, int32_t* cand_idx,
-                       int64_t* cand_tok, float* unary, hipStream_t s) {
-    if (M <= 0) return hipSuccess;
-    const TopkPlan p = topk_plan(M, V, K);
-    hipError_t e;
-    switch (p.per_thread) {
-        case 64: e = launch_chunks<64>(logits, ldz, V, K, M, p.nchunks, chunk_best, s); break;
-        case 32: e = launch_chunks<32>(logits, ldz, V, K, M, p.nchunks, chunk_best, s); break;
-        default: e = launch_chunks<16>(logits, ldz, V, K, M, p.nchunks, chunk_best, s); break;
-    }
-    if (e != hipSuccess) return e;
-    const size_t lds = (size_t)2 * p.nchunks * K * sizeof(uint64_t);
-    hipLaunchKernelGGL(topk_merge_kernel, dim3(M), dim3(kThreads), lds, s, chunk_best, p.nchunks, K, lse,
-                       lse_part, nparts, d2t, V, cand_idx, cand_tok, unary);
-    return hipGetLastError();
-}
 
 // ---------------------------------------------------------------- head-less argmax
 // f(z) = cap tanh(scale z / cap) (cap > 0) or scale z, as head_apply computes it, is
@@ -600,13 +525,61 @@ hipError_t launch_argmax(const float* logits, int64_t ldz, const float* tile_max
 int topk_tiles_chunks(int V) { return (V + kThreads * 64 - 1) / (kThreads * 64); }
 
 hipError_t launch_topk_tiles(const float* logits, int64_t ldz, const float* tile_max, int64_t ldt,
-                             const float2* lse_part, int nparts, const int64_t* d2t, int M, int V, int K,
-                             int32_t* cand_idx, int64_t* cand_tok, float* unary, hipStream_t s) {
+                             const float* lse, const float2* lse_part, int nparts, const int64_t* d2t, int M, int V,
+                             int K, int32_t* cand_idx, int64_t* cand_tok, float* unary, hipStream_t s) {
     if (M <= 0) return hipSuccess;
     const int nchunks = topk_tiles_chunks(V);
     const size_t lds = (size_t)2 * nchunks * K * sizeof(uint64_t);
     hipLaunchKernelGGL(topk_tiles_kernel, dim3(M), dim3(kThreads), lds, s, logits, ldz, tile_max, ldt,
-                       (V + 31) / 32, V, K, nchunks, lse_part, nparts, d2t, cand_idx, cand_tok, unary);
+                       (V + 31) / 32, V, K, nchunks, lse, lse_part, nparts, d2t, cand_idx, cand_tok, unary);
+    return hipGetLastError();
+}
+
+namespace {
+
+// The maximum of every 32-logit tile of every row, in one streaming pass: eight
+// lanes read a tile's 128 bytes with one 16-byte load each (a wave reads 1 KB of
+// contiguous logits per instruction), eight tiles' loads in flight per thread,
+// and the eight lanes combine their maxima with xor shuffles.
+constexpr int kTmU = 8;               // loads in flight per thread
+constexpr int kTmTiles = 32 * kTmU;   // tiles per workgroup
+__global__ void __launch_bounds__(kThreads) tile_max_kernel(const float* __restrict__ logits, int64_t ldz, int V,
+                                                            int tiles, float* __restrict__ tmax, int64_t ldt) {
+    const int m = blockIdx.y;
+    const float* row = logits + (int64_t)m * ldz;
+    const int q8 = threadIdx.x & 7;
+    const int t0 = blockIdx.x * kTmTiles + (threadIdx.x >> 3);
+    f32x4 z[kTmU];
+#pragma unroll
+    for (int u = 0; u < kTmU; ++u) {
+        const int t = t0 + 32 * u;
+        const int v = t * 32 + 4 * q8;
+        // a run of four starting inside the row ends inside its stride (ldz >= V, a multiple of 4)
+        z[u] = (t < tiles && v < V) ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + v))
+                                    : f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    }
+#pragma unroll
+    for (int u = 0; u < kTmU; ++u) {
+        const int t = t0 + 32 * u;
+        const int v = t * 32 + 4 * q8;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) mx = fmaxf(mx, v + q < V ? z[u][q] : -INFINITY);
+        mx = fmaxf(mx, __shfl_xor(mx, 1));
+        mx = fmaxf(mx, __shfl_xor(mx, 2));
+        mx = fmaxf(mx, __shfl_xor(mx, 4));
+        if (q8 == 0 && t < tiles) tmax[(int64_t)m * ldt + t] = mx;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_tile_max(const float* logits, int64_t ldz, int M, int V, float* tile_max, int64_t ldt,
+                           hipStream_t s) {
+    if (M <= 0) return hipSuccess;
+    const int tiles = (V + 31) / 32;
+    hipLaunchKernelGGL(tile_max_kernel, dim3((tiles + kTmTiles - 1) / kTmTiles, M), dim3(kThreads), 0, s, logits,
+                       ldz, V, tiles, tile_max, ldt);
     return hipGetLastError();
 }
 
