@@ -109,7 +109,8 @@ def _topk_feed(z32: np.ndarray, K: int, d2t=None, Vt=None):
     """Run dflash_topk on fp32 logits (with the fp64 LSE of those values rounded to fp32)."""
     M, V = z32.shape
     ldz = V + (-V) % 4
-    zt = torch.zeros((M, ldz), dtype=torch.float32, device="cuda")
+    # the row padding past V holds values above every logit: they must never be read as logits
+    zt = torch.full((M, ldz), 1e30, dtype=torch.float32, device="cuda")
     zt[:, :V] = dev(z32)
     lse = O.row_lse(z32.astype(np.float64))
     idx, tok, un = api().topk(zt[:, :V], dev(f32(lse)), K, d2t=dev(d2t), target_vocab=Vt)
