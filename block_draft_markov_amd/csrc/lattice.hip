@@ -179,7 +179,7 @@ __global__ void __launch_bounds__(kWalkThreads) walk_kernel(const int64_t* __res
     __shared__ int path[DFLASH_MAX_BLOCK_LEN];
     __shared__ float s_score;
     const int req = blockIdx.x, tid = threadIdx.x;
-    const int lane = tid & 63, q = tid >> 6;
+    const int lane = tid & 63, q = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform quarter
     int a, n;
     row_range(row_offsets, req, L, M, a, n);
     if (n <= 0) {
