@@ -135,6 +135,8 @@ TOPK_CASES = [
     ("k1", 4, 5000, 1, "normal"),
     ("v_eq_k", 3, 48, 48, "normal"),         # K = V_d: the 48-token draft vocabulary
     ("v_lt_chunk", 3, 300, 64, "normal"),    # a single short chunk
+    ("v1", 3, 1, 1, "normal"),               # a one-token vocabulary: one partial tile of one logit
+    ("v17", 2, 17, 17, "normal"),            # K = V_d inside one partial tile; V % 4 != 0
     ("ragged_v", 6, 70001, 64, "normal"),    # V % 4 != 0, last chunk partial
     ("ties_small_ints", 5, 9000, 64, "ints"),     # many exact ties: the radix fallback
     ("all_equal", 3, 5000, 64, "equal"),          # every logit equal: slots 0..K-1
@@ -405,6 +407,14 @@ def test_end_to_end_gated_tiny_and_ragged():
     inp.row_offsets = di.ragged_offsets([6, 0, 2, 5])
     inp.hidden = inp.hidden[:13].copy()
     _end_to_end(inp, range(4))
+
+
+@pytest.mark.parametrize("name,Vd,K", [("vocab_1", 1, 1), ("vocab_17", 17, 17), ("vocab_33_k8", 33, 8)])
+def test_end_to_end_tiny_vocabularies(name, Vd, K):
+    """Vocabularies of one partial tile or two: every kernel of the fused step at its edge."""
+    say(f"end-to-end {name}: V={Vd} K={K}")
+    sh = di.custom_shape(name, R=3, L=4, H=64, Vd=Vd, K=K, r=8, table_std=0.5, seed=80 + Vd)
+    _end_to_end(di.make_inputs(sh), [0, 1, 2])
 
 
 def test_end_to_end_pruned_small_48():
