@@ -53,7 +53,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         log(f"bench.py measures the draft step on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
-            "the draft step is not sharded across GPUs in this build.")
+            "the draft step runs on one GPU and is not sharded across GPUs.")
         sys.exit(2)
 
     import numpy as np
