@@ -176,6 +176,7 @@ __global__ void __launch_bounds__(kWalkThreads) walk_kernel(const int64_t* __res
     __shared__ float qbest[2][4][64];
     __shared__ int qarg[2][4][64];
     __shared__ uint8_t back[DFLASH_MAX_BLOCK_LEN][64];
+    __shared__ __attribute__((aligned(16))) float dsh[4][64];   // delta of the previous position, one row per wave
     __shared__ int path[DFLASH_MAX_BLOCK_LEN];
     __shared__ float s_score;
     const int req = blockIdx.x, tid = threadIdx.x;
@@ -244,22 +245,35 @@ __global__ void __launch_bounds__(kWalkThreads) walk_kernel(const int64_t* __res
                 if (p == 0) {
                     d = act ? Us[buf][0][lane] + Ss[buf][0][lane] : -INFINITY;
                 } else {
-                    float best = -INFINITY;
-                    int arg = 16 * q;
-                    // the 16 S entries of this quarter first (their LDS reads overlap), then
-                    // the max in ascending j with strict >, so the lowest j wins a tie
-                    float sv[16];
+                    // the 16 S entries of this quarter and the 16 delta(j) first (independent
+                    // LDS reads and readlanes), then a tree over (value, j) in which the
+                    // higher j wins only by strict >: the lowest j reaching the maximum, as an
+                    // ascending scan with strict > (slots past K are -inf)
+                    float sv[16], vv[16];
+                    int jj[16];
+                    // delta(j) of the quarter reaches every lane through the wave's own LDS row
+                    // (one write, four broadcast reads): in-order LDS access within a wave
+                    // needs no barrier
+                    dsh[q][lane] = d;
 #pragma unroll
                     for (int t = 0; t < 16; ++t) sv[t] = Ss[buf][pp][(16 * q + t) * 64 + lane];
+                    const f32x4* drow = reinterpret_cast<const f32x4*>(&dsh[q][16 * q]);
+                    const f32x4 d0 = drow[0], d1 = drow[1], d2 = drow[2], d3 = drow[3];
+                    const float dq[16] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3],
+                                          d2[0], d2[1], d2[2], d2[3], d3[0], d3[1], d3[2], d3[3]};
 #pragma unroll
                     for (int t = 0; t < 16; ++t) {
                         const int j = 16 * q + t;
-                        if (j < K) {
-                            const float dj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(d), j));
-                            const float v = dj + sv[t];
-                            if (v > best) { best = v; arg = j; }
-                        }
+                        vv[t] = j < K ? dq[t] + sv[t] : -INFINITY;
+                        jj[t] = j;
                     }
+#pragma unroll
+                    for (int w = 1; w < 16; w *= 2)
+#pragma unroll
+                        for (int t = 0; t < 16; t += 2 * w)
+                            if (vv[t + w] > vv[t]) { vv[t] = vv[t + w]; jj[t] = jj[t + w]; }
+                    const float best = vv[0];
+                    const int arg = jj[0];
                     qbest[par][q][lane] = best;
                     qarg[par][q][lane] = arg;
                     __syncthreads();
