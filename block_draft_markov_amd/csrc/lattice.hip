@@ -259,6 +259,8 @@ __global__ void __launch_bounds__(kWalkThreads) walk_kernel(const int64_t* __res
                     for (int t = 0; t < 16; ++t) sv[t] = Ss[buf][pp][(16 * q + t) * 64 + lane];
                     const f32x4* drow = reinterpret_cast<const f32x4*>(&dsh[q][16 * q]);
                     const f32x4 d0 = drow[0], d1 = drow[1], d2 = drow[2], d3 = drow[3];
+                    // every LDS read above is issued before the first sum below uses one
+                    __builtin_amdgcn_sched_barrier(0);
                     const float dq[16] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3],
                                           d2[0], d2[1], d2[2], d2[3], d3[0], d3[1], d3[2], d3[3]};
 #pragma unroll
