@@ -64,6 +64,24 @@ __device__ __forceinline__ int block_excl_scan(int v, int* wsum, int& total) {
 __device__ __forceinline__ void rank_place(const uint64_t* list, int n, int K, uint64_t* out) {
     const ulonglong2* pairs = reinterpret_cast<const ulonglong2*>(list);
     const int np = (n + 1) >> 1;
+    if (n <= kThreads / 2) {
+        // two threads per entry, each counting the better entries in one half of the pairs
+        const int i = threadIdx.x >> 1, h = threadIdx.x & 1;
+        const uint64_t my = i < n ? list[i] : 0;
+        const int half = (np + 1) >> 1;
+        const int j0 = h * half, j1 = min(np, j0 + half);
+        int rank = 0;
+#pragma unroll 4
+        for (int j = j0; j < j1; ++j) {
+            const ulonglong2 e = pairs[j];
+            rank += (e.x > my) ? 1 : 0;
+            rank += (e.y > my) ? 1 : 0;
+        }
+        rank += __shfl_xor(rank, 1);
+        if (i < n && h == 0 && rank < K) out[rank] = my;
+        for (int k = n + threadIdx.x; k < K; k += kThreads) out[k] = kEmptyEntry;
+        return;
+    }
     for (int i = threadIdx.x; i < n; i += kThreads) {
         const uint64_t my = list[i];
         int rank = 0;
@@ -223,13 +241,6 @@ __device__ __forceinline__ int count_better(const uint64_t* y, int n, uint64_t x
     return lo;
 }
 
-// lse of row m from the (max, sum exp) partials, or the given value; the same for every thread.
-__device__ __forceinline__ float row_lse_value(int m, const float* lse_in, const float2* lse_part, int nparts,
-                                              float2* red) {
-    if (lse_part) return block_lse(lse_part, m, nparts, red);
-    return lse_in[m];
-}
-
 // Merge nl slot-ordered lists of K entries held in LDS at a[0 .. nl K) (b is
 // scratch of the same size) pairwise into one; returns the buffer holding it.
 __device__ __forceinline__ uint64_t* merge_lists(uint64_t* a, uint64_t* b, int nl, int K) {
@@ -283,7 +294,8 @@ __device__ __forceinline__ void write_row(const uint64_t* list, int m, int K, in
 // logits (heavy ties) takes the exact path over all its logits instead.
 constexpr int kSelCap = 1024;
 constexpr int kCandCap = 512;
-constexpr int kTileCap = 8192;   // tile-maxima keys kept in LDS (32 KB); longer rows re-read them
+constexpr int kTileCap = 8192;   // tile-maxima keys kept in registers (32 per thread); longer rows re-read the rest
+constexpr int kPartCap = 2048;   // lse partials loaded with the tile maxima (8 per thread); more are merged later
 
 __global__ void __launch_bounds__(kThreads) topk_tiles_kernel(const float* __restrict__ logits, int64_t ldz,
                                                               const float* __restrict__ tmax, int64_t ldt,
@@ -296,7 +308,6 @@ __global__ void __launch_bounds__(kThreads) topk_tiles_kernel(const float* __res
                                                               float* __restrict__ unary) {
     extern __shared__ uint64_t lists[];   // exact path: 2 * nchunks * K entries
     __shared__ ChunkShared sh;
-    __shared__ uint32_t tkey[kTileCap];   // keys of the tile maxima (rows of at most kTileCap tiles)
     __shared__ int sel[kSelCap];
     __shared__ __attribute__((aligned(16))) uint64_t cand[kCandCap + 2];
     __shared__ uint64_t top[kMaxTopK];
@@ -306,29 +317,76 @@ __global__ void __launch_bounds__(kThreads) topk_tiles_kernel(const float* __res
     const int m = blockIdx.x;
     const float* row = logits + (int64_t)m * ldz;
     const float* trow = tmax + (int64_t)m * ldt;
-    const bool staged = tiles <= kTileCap;
-
-    // ---- the first kTileCap tile maxima are loaded before the lse partials, so that both
-    // sets of loads are in flight together; rows with more tiles loop over the rest
+    // ---- loads: the first kPartCap lse partials (or the caller's lse), then the first
+    // kTileCap tile maxima, which are still in flight while the partials are merged
     constexpr int kTPT = kTileCap / kThreads;   // tile maxima per thread in the first round
+    constexpr int kPPT = kPartCap / kThreads;   // lse partials per thread in the first round
+    const float2* prow = lse_part ? lse_part + (int64_t)m * nparts : nullptr;
+    // Every load below is issued by every lane (indices past the end are clamped and the
+    // value replaced), so that the compiler can count the tile-maxima loads as issued after
+    // the partials and wait for the partials alone.
+    float2 pv[kPPT];
+    if (prow) {
+#pragma unroll
+        for (int i = 0; i < kPPT; ++i) {
+            const int idx = tid + kThreads * i;
+            const float2 x = prow[idx < nparts ? idx : nparts - 1];
+            pv[i] = idx < nparts ? x : make_float2(0.f, 0.f);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < kPPT; ++i) pv[i] = make_float2(0.f, 0.f);
+    }
+    const float lse_given = lse_part ? 0.f : lse_in[m];
     float tv[kTPT];
 #pragma unroll
     for (int i = 0; i < kTPT; ++i) {
         const int t = tid + kThreads * i;
-        tv[i] = t < tiles ? trow[t] : 0.f;
+        const float x = trow[t < tiles ? t : tiles - 1];
+        tv[i] = t < tiles ? x : 0.f;
     }
-    const float lse = row_lse_value(m, lse_in, lse_part, nparts, red);
+    // The lse is merged in two halves: each wave's (max, sum exp) into red[], then the four
+    // waves after the next barrier.  The order of the merges is that of block_lse, so the
+    // value is the same bit for bit.
+    auto lse_wave = [&]() __attribute__((always_inline)) {
+        if (!prow) return;
+        float a = 0.f, sm = 0.f;
+#pragma unroll
+        for (int i = 0; i < kPPT; ++i) lse_merge(a, sm, pv[i].x, pv[i].y);
+        for (int base = kPartCap; base < nparts; base += kPartCap) {
+            float2 v[kPPT];
+#pragma unroll
+            for (int i = 0; i < kPPT; ++i) {
+                const int idx = base + tid + kThreads * i;
+                v[i] = idx < nparts ? prow[idx] : make_float2(0.f, 0.f);
+            }
+#pragma unroll
+            for (int i = 0; i < kPPT; ++i) lse_merge(a, sm, v[i].x, v[i].y);
+        }
+        for (int o = 32; o > 0; o >>= 1) {
+            const float m2 = __shfl_xor(a, o);
+            const float s2 = __shfl_xor(sm, o);
+            lse_merge(a, sm, m2, s2);
+        }
+        if ((tid & 63) == 0) red[tid >> 6] = make_float2(a, sm);
+    };
+    auto lse_final = [&]() __attribute__((always_inline)) {   // after a barrier that follows lse_wave
+        if (!prow) return lse_given;
+        float a = 0.f, sm = 0.f;
+        for (int w = 0; w < 4; ++w) lse_merge(a, sm, red[w].x, red[w].y);
+        return a + logf(sm);
+    };
 
-    // ---- tau from the tile maxima
+    lse_wave();
+
+    // ---- tau from the tile maxima; their keys stay in registers
+    uint32_t kv[kTPT];
     uint32_t mx = 0;
 #pragma unroll
     for (int i = 0; i < kTPT; ++i) {
         const int t = tid + kThreads * i;
-        if (t < tiles) {
-            const uint32_t k = float_to_key(tv[i]);
-            mx = max(mx, k);
-            tkey[t] = k;
-        }
+        kv[i] = t < tiles ? float_to_key(tv[i]) : 0u;   // 0 is below every tau
+        mx = max(mx, kv[i]);
     }
     for (int t = kTileCap + tid; t < tiles; t += kThreads) mx = max(mx, float_to_key(trow[t]));
     const uint32_t sorted = wave_sort_desc(mx);
@@ -338,13 +396,37 @@ __global__ void __launch_bounds__(kThreads) topk_tiles_kernel(const float* __res
     if (tid == 0) { s_nsel = 0; s_ncand = 0; }
     __syncthreads();
     const uint32_t tau = max(min(min(sh.wtau[0], sh.wtau[1]), min(sh.wtau[2], sh.wtau[3])), 1u);
+    const float lse = lse_final();
 
-    // ---- the tiles that may hold a member of the top K
-    for (int t = tid; t < tiles; t += kThreads) {
-        const uint32_t k = staged ? tkey[t] : float_to_key(trow[t]);
-        if (k >= tau) {
-            const int i = atomicAdd(&s_nsel, 1);
-            if (i < kSelCap) sel[i] = t;
+    // ---- the tiles that may hold a member of the top K: a prefix count over the wave and
+    // one LDS atomic per wave place each thread's tiles in sel[]
+    {
+        int c = 0;
+#pragma unroll
+        for (int i = 0; i < kTPT; ++i) c += kv[i] >= tau ? 1 : 0;
+        const int lane = tid & 63;
+        int x = c;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(x, o);
+            if (lane >= o) x += y;
+        }
+        int base = 0;
+        if (lane == 63 && x > 0) base = atomicAdd(&s_nsel, x);
+        base = __shfl(base, 63);
+        int j = base + x - c;
+#pragma unroll
+        for (int i = 0; i < kTPT; ++i) {
+            if (kv[i] >= tau) {
+                if (j < kSelCap) sel[j] = tid + kThreads * i;
+                ++j;
+            }
+        }
+    }
+    for (int t = kTileCap + tid; t < tiles; t += kThreads) {
+        if (float_to_key(trow[t]) >= tau) {
+            const int j = atomicAdd(&s_nsel, 1);
+            if (j < kSelCap) sel[j] = t;
         }
     }
     __syncthreads();
@@ -353,14 +435,16 @@ __global__ void __launch_bounds__(kThreads) topk_tiles_kernel(const float* __res
     if (!exact) {
         // ---- their logits >= tau (sixteen loads in flight per thread at a time: one round
         // for up to 128 tiles)
-        for (int base = 0; base < nsel * 32; base += kThreads * 16) {
-            float zv[16];
+        float zv[16];
+        auto load_round = [&](int base) __attribute__((always_inline)) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int e = base + tid + kThreads * i;
                 const int v = e < nsel * 32 ? sel[e >> 5] * 32 + (e & 31) : V;
                 zv[i] = v < V ? row[v] : 0.f;
             }
+        };
+        auto scan_round = [&](int base) __attribute__((always_inline)) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int e = base + tid + kThreads * i;
@@ -373,6 +457,10 @@ __global__ void __launch_bounds__(kThreads) topk_tiles_kernel(const float* __res
                     }
                 }
             }
+        };
+        for (int base = 0; base < nsel * 32; base += kThreads * 16) {
+            load_round(base);
+            scan_round(base);
         }
         __syncthreads();
         const int n = s_ncand;
