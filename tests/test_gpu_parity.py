@@ -144,6 +144,8 @@ TOPK_CASES = [
     ("qwen3_4b_rows", 4, 151936, 64, "normal"),
     ("dflash2_27b_rows", 3, 248100, 64, "normal"),
     ("many_rows", 224, 151936, 64, "normal"),     # the row count of the 4B batch: the large-chunk plan
+    ("long_row", 2, 300000, 64, "normal"),        # 9375 tiles: more than the 8192 tile maxima kept in registers
+    ("long_row_ties", 2, 300000, 64, "ints"),     # the same length with heavy ties: the exact path
 ]
 
 
@@ -448,6 +450,7 @@ def _zero_hidden(inp):
     ("batched_ragged_vocab", 20, 5, 5003, False),    # tile maxima path, partial last tile
     ("batched_ties_all_tiles", 13, 7, 40000, True),  # every tile ties: more than 1024 tiles kept -> exact path
     ("batched_ties_candidates", 17, 5, 3000, True),  # 94 tiles kept but 3000 tied logits -> exact path
+    ("batched_long_rows", 10, 7, 300000, False),     # 9375 tiles per row: past the 8192 kept in registers
 ])
 def test_end_to_end_batched_tile_maxima_paths(name, R, L, V, zero):
     """More than 64 rows: the Top-K reads only the tiles the lm_head tile maxima keep,
