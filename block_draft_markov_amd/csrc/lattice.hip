@@ -36,7 +36,8 @@ namespace dflash {
 
 namespace {
 
-constexpr int kPairThreads = 256;
+constexpr int kPairThreads = 512;   // eight waves: two per quadrant of S, one per half of the rank
+constexpr int kGateThreads = 256;   // threads of the gate's dot product
 constexpr int kRankSlice = 256;   // rank elements staged per round
 constexpr int kPitch = kRankSlice + 4;   // LDS row pitch (floats): 16 consecutive rows hit distinct banks
 
@@ -65,7 +66,7 @@ __global__ void __launch_bounds__(kPairThreads) pair_scores_kernel(
     __shared__ __attribute__((aligned(16))) float As[64][kPitch];
     __shared__ __attribute__((aligned(16))) float Bs[64][kPitch];
     __shared__ int64_t prev_row[64], cand_row[64];
-    __shared__ float red[4];
+    __shared__ float red[kGateThreads / 64];
 
     const int p = blockIdx.x, req = blockIdx.y;
     const int tid = threadIdx.x;
@@ -86,9 +87,11 @@ __global__ void __launch_bounds__(kPairThreads) pair_scores_kernel(
     if (gate_w) {
         float part = 0.f;
         const uint16_t* h = hidden + (int64_t)m * H;
-        for (int i = tid; i < H; i += kPairThreads) part += gate_w[i] * bf16_bits_to_float(h[i]);
-        part = wave_sum(part);
-        if ((tid & 63) == 0) red[tid >> 6] = part;
+        if (tid < kGateThreads) {
+            for (int i = tid; i < H; i += kGateThreads) part += gate_w[i] * bf16_bits_to_float(h[i]);
+            part = wave_sum(part);
+            if ((tid & 63) == 0) red[tid >> 6] = part;
+        }
     }
     __syncthreads();
     if (gate_w) {
@@ -98,13 +101,16 @@ __global__ void __launch_bounds__(kPairThreads) pair_scores_kernel(
 
     const float* TA = tables;
     const float* TB = tables + (int64_t)Vt * r;
-    // wave w computes the 32 x 32 quadrant (jt, kt) = (w / 2, w % 2) of S on the matrix
-    // cores (v_mfma_f32_32x32x2_f32, fp32 products and sums): in MFMA step s lane l
-    // supplies A[prev 32 jt + l % 32][k] and B[cand 32 kt + l % 32][k] with k = 8 (s / 4)
-    // + 4 (l / 32) + s % 4, the same in both, read as float4 from the LDS rows
-    const int lane = tid & 63, wv = tid >> 6;
+    // waves w and w + 4 compute the 32 x 32 quadrant (jt, kt) = ((w % 4) / 2, w % 2) of S
+    // on the matrix cores (v_mfma_f32_32x32x2_f32, fp32 products and sums), over the first
+    // and the second half of every rank slice: in MFMA step s lane l supplies
+    // A[prev 32 jt + l % 32][k] and B[cand 32 kt + l % 32][k] with k = 8 (s / 4) + 4 (l / 32)
+    // + s % 4, the same in both, read as float4 from the LDS rows; the two partial sums
+    // are added once at the end (first half + second half)
+    const int lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lr = lane & 31, lh = lane >> 5;
-    const int jt = wv >> 1, kt = wv & 1;
+    const int quad = wv & 3, half = wv >> 2;
+    const int jt = quad >> 1, kt = quad & 1;
     f32x16 acc = f32x16{};
 
     // With r % 4 == 0 and 16-byte aligned tables every row is read as float4:
@@ -113,9 +119,10 @@ __global__ void __launch_bounds__(kPairThreads) pair_scores_kernel(
     for (int i0 = 0; i0 < r; i0 += kRankSlice) {
         const int w = min(kRankSlice, r - i0);        // rank elements of this slice
         if (vec) {
-            f32x4 v[32];
+            constexpr int kPer = 2 * 64 * kRankSlice / 4 / kPairThreads;   // float4 per thread
+            f32x4 v[kPer];
 #pragma unroll
-            for (int i = 0; i < 32; ++i) {
+            for (int i = 0; i < kPer; ++i) {
                 const int f = tid + i * kPairThreads;       // 0 .. 8191
                 const int b = f >> 12, row = (f >> 6) & 63, c = (f & 63) * 4;
                 const bool ok = row < (b ? K : Jn) && c < w;
@@ -123,7 +130,7 @@ __global__ void __launch_bounds__(kPairThreads) pair_scores_kernel(
                 v[i] = ok ? *reinterpret_cast<const f32x4*>(src) : f32x4{0.f, 0.f, 0.f, 0.f};
             }
 #pragma unroll
-            for (int i = 0; i < 32; ++i) {
+            for (int i = 0; i < kPer; ++i) {
                 const int f = tid + i * kPairThreads;
                 const int b = f >> 12, row = (f >> 6) & 63, c = (f & 63) * 4;
                 *reinterpret_cast<f32x4*>(b ? &Bs[row][c] : &As[row][c]) = v[i];
@@ -138,9 +145,10 @@ __global__ void __launch_bounds__(kPairThreads) pair_scores_kernel(
         }
         __syncthreads();
         const int w8 = (w + 7) >> 3;                  // elements past w are zero in both operands
+        const int gmid = (w8 + 1) >> 1;
         const float* arow = &As[32 * jt + lr][4 * lh];
         const float* brow = &Bs[32 * kt + lr][4 * lh];
-        for (int gi = 0; gi < w8; ++gi) {
+        for (int gi = half ? gmid : 0; gi < (half ? w8 : gmid); ++gi) {
             const f32x4 av = *reinterpret_cast<const f32x4*>(arow + 8 * gi);
             const f32x4 bv = *reinterpret_cast<const f32x4*>(brow + 8 * gi);
 #pragma unroll
@@ -148,6 +156,18 @@ __global__ void __launch_bounds__(kPairThreads) pair_scores_kernel(
         }
         __syncthreads();
     }
+
+    // the second-half waves hand their sums to the first-half waves through LDS (As is
+    // free after the last slice's barrier): register i of lane l at float 1024 quad + 64 i + l
+    float* xch = &As[0][0];
+    if (half) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) xch[1024 * quad + 64 * i + lane] = acc[i];
+    }
+    __syncthreads();
+    if (half) return;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] += xch[1024 * quad + 64 * i + lane];
 
     // register i of lane l: S[32 jt + 8 (i / 4) + 4 (l / 32) + i % 4][32 kt + l % 32]
     float* out = pair + (int64_t)m * K * K;
