@@ -154,13 +154,14 @@ lmhead_dma_kernel(LmHeadArgs a) {
     const int npass = nfull + (rest > 0);
     const int nv_last = rest <= 4 ? 1 : NV;
     const int split = nv_last == 1 && rest > 0 ? nfull : npass;   // passes before the one-tile pass
-    // The one-tile pass runs first, after the first full pass or last, by workgroup (b % 3),
-    // so that the logits stores at the ends of passes are not issued by every CU at the same
-    // moment (three phases measured 3 us faster than two).  sp: its position in the
-    // workgroup's stream of passes.
-    const int sp = split >= npass ? npass : (b % 3 == 1 ? 0 : (b % 3 == 2 ? min(1, split) : split));
+    // The last, partly filled pass (one tile per wave, or NV tiles for some waves) runs
+    // first, after the first full pass or last, by workgroup (b % 3), so that the logits
+    // stores at the ends of passes are not issued by every CU at the same moment.  lastp:
+    // its logical index; sp: its position in the workgroup's stream of passes.
+    const int lastp = rest > 0 ? nfull : npass;
+    const int sp = lastp >= npass ? npass : (b % 3 == 1 ? 0 : (b % 3 == 2 ? min(1, lastp) : lastp));
     auto stream_pass = [&](int q) __attribute__((always_inline)) {   // logical pass of stream position q
-        return split >= npass ? q : (q < sp ? q : (q == sp ? split : q - 1));
+        return lastp >= npass ? q : (q < sp ? q : (q == sp ? lastp : q - 1));
     };
     auto pass_first = [&](int p) __attribute__((always_inline)) {
         const int nv = p < nfull ? NV : nv_last;
@@ -392,8 +393,11 @@ lmhead_dma_kernel(LmHeadArgs a) {
             }
         };
         if (sp > 0) run(std::integral_constant<int, NV>{}, 0, sp);
-        if (split < npass) run(std::integral_constant<int, 1>{}, split, npass);
-        if (sp < split) run(std::integral_constant<int, NV>{}, sp, split);
+        if (lastp < npass) {
+            if (split < npass) run(std::integral_constant<int, 1>{}, lastp, npass);
+            else run(std::integral_constant<int, NV>{}, lastp, npass);
+        }
+        if (sp < lastp) run(std::integral_constant<int, NV>{}, sp, lastp);
         // the loads issued past the last step write LDS: let them land before the workgroup ends
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     }
