@@ -47,6 +47,7 @@ SIGNATURES = {
     "dflash_topk": (ctypes.c_int, [_PD, _P, _I64, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "dflash_pair_scores": (ctypes.c_int, [_PD, _P, _P, _P, _P, _P, _P, _P, _P]),
     "dflash_walk": (ctypes.c_int, [_PD, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "dflash_lattice": (ctypes.c_int, [_PD, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "dflash_draft_argmax": (ctypes.c_int, [_PD, _P, _P, _P, ctypes.c_float, ctypes.c_float, _P, _P, _P, _SZ, _P]),
     "dflash_draft_dense": (ctypes.c_int, [_PD, _P, _P, _P, _P, _P, _P, ctypes.c_float, ctypes.c_float, _P, _P, _P,
                                           _SZ, _P]),

@@ -397,6 +397,31 @@ int dflash_walk(const dflash_dims* d, const int64_t* cand_tok, const float* unar
     return ok();
 }
 
+int dflash_lattice(const dflash_dims* d, const int64_t* cand_tok, const float* unary, const float* tables,
+                   const float* gate_w, const uint16_t* hidden, const int64_t* last_tok, const int32_t* row_offsets,
+                   int64_t* tokens, float* scores, void* ws, size_t ws_bytes, void* stream) {
+    int rc;
+    if ((rc = check_dims(d)) || (rc = check_rows(d, row_offsets))) return rc;
+    const int64_t M = d->total_rows, R = d->num_requests;
+    if ((rc = need(cand_tok, M, "cand_tok")) || (rc = need(unary, M, "unary")) || (rc = need(tables, 1, "tables")) ||
+        (rc = need(last_tok, R, "last_tok")) || (rc = need(tokens, M, "tokens")) || (rc = need(scores, R, "scores")))
+        return rc;
+    if (gate_w && (rc = need(hidden, M, "hidden (read by the gate)"))) return rc;
+    Layout l;
+    if ((rc = check_ws(d, ws, ws_bytes, l))) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    float* pair = at<float>(ws, l.pair);
+    if ((e = dflash::launch_pair_scores(cand_tok, tables, gate_w, hidden, last_tok, row_offsets, d->num_requests,
+                                        d->block_len, d->total_rows, d->hidden, d->target_vocab, d->top_k, d->rank,
+                                        pair, s)) != hipSuccess)
+        return hip_fail(e, "pair-score launch");
+    if ((e = dflash::launch_walk(cand_tok, unary, pair, row_offsets, d->num_requests, d->block_len, d->total_rows,
+                                 d->top_k, d->walk, tokens, scores, nullptr, s)) != hipSuccess)
+        return hip_fail(e, "walk launch");
+    return ok();
+}
+
 int dflash_walk_sampled(const dflash_dims* d, const int64_t* cand_tok, const float* unary, const float* pair,
                         const int32_t* row_offsets, const double* uniforms, float temperature, int64_t* tokens,
                         float* scores, int32_t* slots, double* q, void* stream) {

@@ -31,14 +31,8 @@ constexpr int kGroup = 32;     // requests per workgroup
 constexpr int kBufWord3 = 0x00020000;   // gfx9 buffer descriptor word 3: raw dword access
 constexpr int kBig = 0x40000000;        // buffer offset past the end of every table the buffer path takes
 constexpr int kRankChunk = 256; // rank elements of the A rows staged in LDS at a time
-#ifndef DENSE_AHEAD
-#define DENSE_AHEAD 1
-#endif
-#ifndef DENSE_TPW
-#define DENSE_TPW 3
-#endif
-constexpr int kAhead = DENSE_AHEAD;   // 32-element slots of B in flight ahead of the MFMAs
-constexpr int kTpw = DENSE_TPW;       // 32-id vocab tiles per wave
+constexpr int kAhead = 1;   // 32-element slots of B in flight ahead of the MFMAs
+constexpr int kTpw = 3;     // 32-id vocab tiles per wave (one, two and four measured slower)
 constexpr int kIds = 4 * 32 * kTpw;   // vocab ids per workgroup
 constexpr int kAStride = kRankChunk + 4;   // padded row stride: the 32 rows of a read hit distinct banks
 

@@ -121,27 +121,44 @@ int dflash_draft_block(const dflash_dims* dims,
                        int64_t* tokens, float* scores,
                        void* workspace, size_t workspace_bytes, void* stream);
 
-/* Part 1: logits[m][v] (fp32, row stride ldz >= V_d, ldz % 4 == 0) of every row
- * and lse[m] (fp32 [M], or NULL to skip it), from bf16 hidden [M][H] and
- * lm_head [V_d][H].  The per-row (max, sum exp) partials stay in the workspace. */
+/* Part 1 (optimum-intel page "Support MiniCPM-OCR-1.0-DSpark", What does this
+ * PR do?: the draft applies its own lm_head and outputs logits over the draft
+ * vocabulary): logits[m][v] (fp32, row stride ldz >= V_d, ldz % 4 == 0) of
+ * every row and lse[m] (fp32 [M], or NULL to skip it), from bf16 hidden [M][H]
+ * and lm_head [V_d][H].  The per-row (max, sum exp) partials stay in the
+ * workspace; logits and lse are caller-owned outputs. */
 int dflash_lm_head(const dflash_dims* dims, const uint16_t* hidden, const uint16_t* lm_head,
                    float* logits, int64_t ldz, float* lse,
                    void* workspace, size_t workspace_bytes, void* stream);
 
-/* lse[m] = log sum_v exp logits[m][v] over the first V_d entries of every row
- * (row stride ldz), for logits that did not come from dflash_lm_head. */
+/* The unary's normaliser (the log-softmax over the draft vocabulary, the
+ * reading of optimum-intel page "Support MiniCPM-OCR-1.0-DSpark", Tests: the
+ * reference scores over the draft vocabulary): lse[m] = log sum_v exp
+ * logits[m][v] over the first V_d entries of every row (row stride ldz >= V_d),
+ * for logits that did not come from dflash_lm_head.  No workspace. */
 int dflash_row_lse(const dflash_dims* dims, const float* logits, int64_t ldz, float* lse,
                    void* stream);
 
-/* Part 2: the K slots of every row in slot order.
- *   logits fp32 [M][ldz], lse fp32 [M], d2t int64 [V_d] or NULL
+/* Part 2 (optimum-intel page "Export DFlash v2 and DSpark drafts ...", What
+ * does this PR do?: the radix TopK of the head; optimum-intel page "Support
+ * MiniCPM-OCR-1.0-DSpark", What does this PR do?: K = min(64, draft vocabulary)
+ * and draft token i -> target token i + d2t[i]; ties ordered by index as in the
+ * TopP commit of the openvino.genai page): the K slots of every row in slot
+ * order (logit descending, draft id ascending).
+ *   logits fp32 [M][ldz] (ldz >= V_d, ldz % 4 == 0, 16-byte aligned),
+ *   lse fp32 [M], d2t int64 [V_d] or NULL (needed when V_t > V_d)
  *   cand_idx out int32 [M][K] draft ids; cand_tok out int64 [M][K] target ids;
  *   unary out fp32 [M][K] = z - lse. */
 int dflash_topk(const dflash_dims* dims, const float* logits, int64_t ldz, const float* lse,
                 const int64_t* d2t, int32_t* cand_idx, int64_t* cand_tok, float* unary,
                 void* workspace, size_t workspace_bytes, void* stream);
 
-/* Part 3: transition scores of every row, out fp32 pair [M][K][K]:
+/* Part 3 (optimum-intel page "Export DFlash v2 and DSpark drafts ...", What
+ * does this PR do?: the Top-K lattice, transitions gated by the draft hidden
+ * states for DFlash v2; openvino.genai page "Add DSpark and DFlash v2 drafts
+ * ...", commit "DFlash-2 Markov head / BlockRowSource": one scorer run over
+ * the packed rows of all requests): transition scores of every row, out fp32
+ * pair [M][K][K] (caller-owned, no workspace):
  * pair[m(p)][j][k] = S_p[j][k] for p >= 1; for p = 0 row j = 0 holds S_0[0][k]
  * and rows j >= 1 are written as 0.
  *   cand_tok int64 [M][K], tables fp32 [2][V_t][r], gate_w fp32 [H] or NULL,
@@ -151,13 +168,37 @@ int dflash_pair_scores(const dflash_dims* dims, const int64_t* cand_tok, const f
                        const float* gate_w, const uint16_t* hidden, const int64_t* last_tok,
                        const int32_t* row_offsets, float* pair, void* stream);
 
-/* Part 4: the walk of every request over unary fp32 [M][K] and pair fp32
- * [M][K][K] (as written by dflash_pair_scores), one launch for all requests.
+/* Part 4 (openvino.genai page "Add DSpark and DFlash v2 drafts ...", commit
+ * "DFlash-2 Markov head / BlockRowSource": the greedy walk takes the best
+ * candidate after the token before; the max-score walk is its Viterbi form):
+ * the walk of every request over unary fp32 [M][K] and pair fp32 [M][K][K] (as
+ * written by dflash_pair_scores), one launch for all requests, no workspace.
  *   tokens out int64 [M] = cand_tok[m][c_p]; scores out fp32 [R];
  *   slots out int32 [M] (the chosen slot c_p of every row) or NULL. */
 int dflash_walk(const dflash_dims* dims, const int64_t* cand_tok, const float* unary,
                 const float* pair, const int32_t* row_offsets,
                 int64_t* tokens, float* scores, int32_t* slots, void* stream);
+
+/* Parts 3 and 4 in one call: the candidate scorer over the packed block rows
+ * of all requests, then the walk (openvino.genai page "Add DSpark and DFlash
+ * v2 drafts ...", commit "DFlash-2 Markov head / BlockRowSource": the Top-K
+ * scorer runs once over the packed rows of every scheduled request and the
+ * walk then takes the candidates request by request).
+ *   cand_tok    int64 [M][K] target ids of the slots (slot order, as dflash_topk writes)
+ *   unary       fp32 [M][K] unary score of every slot
+ *   tables      fp32 [2][V_t][r]; gate_w fp32 [H] or NULL; hidden bf16 [M][H]
+ *               (read only when gate_w is given, may be NULL otherwise)
+ *   last_tok    int64 [R]; row_offsets int32 [R+1] or NULL
+ *   tokens      out int64 [M] = cand_tok[m][c_p]; scores out fp32 [R] (0 for a
+ *               request without rows)
+ *   workspace   dflash_workspace_bytes(dims) bytes, 256-byte aligned; holds S
+ * dims->draft_vocab only bounds top_k here.  Token ids must lie in [0, V_t)
+ * (the kernels clamp them).  Same results as dflash_pair_scores followed by
+ * dflash_walk, bit for bit. */
+int dflash_lattice(const dflash_dims* dims, const int64_t* cand_tok, const float* unary, const float* tables,
+                   const float* gate_w, const uint16_t* hidden, const int64_t* last_tok,
+                   const int32_t* row_offsets, int64_t* tokens, float* scores,
+                   void* workspace, size_t workspace_bytes, void* stream);
 
 /* Sampled drafting (openvino.genai page "Add DSpark and DFlash v2 drafts and
  * sampled drafting ...", commit "DFlash-2 Markov head / BlockRowSource": a

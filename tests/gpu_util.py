@@ -73,33 +73,47 @@ def logits_tol(z_orc_row: np.ndarray) -> float:
     return 1e-3 * float(np.max(np.abs(z_orc_row)))
 
 
-def check_topk_row(gpu_idx: np.ndarray, z_orc_row: np.ndarray, K: int):
-    """Top-K set rule.  Returns 'exact' or 'exempt'; raises AssertionError on a violation.
+def check_topk_row(gpu_idx: np.ndarray, z_orc_row: np.ndarray, K: int) -> str:
+    """Top-K set rule for one row.  Raises AssertionError on a violation; returns
 
-    With tau = 1e-3 max|z| and v_1 >= v_2 >= ... the oracle's sorted row: if
-    v_K - v_{K+1} >= tau the GPU slot set must equal the oracle's (and the
-    slots be in logit order up to 1e-5 max|z|).
-    Otherwise every id with z > v_{K+1} + tau must be among the GPU slots and
-    every GPU slot must have z >= v_K - tau.
+      'same'    the GPU slots are the oracle's slots, in the oracle's order;
+      'reorder' the same K ids, in another order (only ids within the fine
+                tolerance of each other may swap);
+      'differs' another set: allowed only where the oracle's K-th and (K+1)-th
+                logits are closer than tau = 1e-3 max|z| (the Top-K boundary
+                exemption), and then every id with z > v_{K+1} + tau must be
+                among the GPU slots and every GPU slot must have z >= v_K - tau.
+
+    Stricter than the bar: the fp32 logits are within ~1e-6 relative, so a gap
+    of 1e-5 max|z| (`fine`) already decides the set.
     """
     order = O.topk_slots(z_orc_row, min(K + 1, z_orc_row.size))
     tau = logits_tol(z_orc_row)
     vK = z_orc_row[order[K - 1]]
     vK1 = z_orc_row[order[K]] if z_orc_row.size > K else -np.inf
-    fine = 1e-2 * tau    # ~1e-5 max|z|: well above the fp32 error of the GPU logits (~1e-6 relative)
-    # slot order: non-increasing in the oracle's logits up to the fine tolerance
+    fine = 1e-2 * tau
+    ids = gpu_idx.tolist()
+    assert len(set(ids)) == K, "duplicate GPU slots"
     zg = z_orc_row[gpu_idx]
     assert np.all(zg[:-1] >= zg[1:] - fine), "GPU slots are not in logit order"
-    if vK - vK1 >= tau:
-        assert set(gpu_idx.tolist()) == set(order[:K].tolist()), "Top-K set differs outside the tie tolerance"
-        return "exact"
-    # Stricter than the bar: fp32 logits are within ~1e-6 relative, so a gap of
-    # 1e-5 max|z| already decides the set; the order within it may still differ
-    # only where two candidates are that close.
+    same_set = set(ids) == set(order[:K].tolist())
     if vK - vK1 >= fine:
-        assert set(gpu_idx.tolist()) == set(order[:K].tolist()), "Top-K set differs at a gap above 1e-5 max|z|"
-    must = np.flatnonzero(z_orc_row > vK1 + tau)
-    assert set(must) <= set(gpu_idx.tolist())
-    assert np.all(z_orc_row[gpu_idx] >= vK - tau)
-    assert len(set(gpu_idx.tolist())) == K
-    return "exempt"
+        assert same_set, f"Top-K set differs at a boundary gap of {vK - vK1:.3e} (>= {fine:.3e})"
+    if not same_set:
+        must = np.flatnonzero(z_orc_row > vK1 + tau)
+        assert set(must.tolist()) <= set(ids)
+        assert np.all(zg >= vK - tau)
+        return "differs"
+    return "same" if np.array_equal(gpu_idx, order[:K]) else "reorder"
+
+
+def record(test: str, **counts) -> None:
+    """Append a parity record (a JSON line) to $PARITY_LOG when that variable is set,
+    so that exact and exempt counts survive a quiet pytest run."""
+    import json
+    import os
+    path = os.environ.get("PARITY_LOG")
+    say(f"  {test}: {counts}")
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps(dict(test=test, **counts)) + "\n")

@@ -44,7 +44,7 @@ def err(lib):
 
 def test_every_declared_symbol_is_exported(lib):
     names = header_functions()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     for n in names:
         assert hasattr(lib, n), f"{n} declared in include/ but not exported"
     assert set(names) == set(bdm.SIGNATURES), "binding and header disagree"
@@ -287,3 +287,122 @@ def test_sampled_entry_points_validate(lib):
     assert wlk(uni=None) == bdm.EINVAL and "uniforms" in err(lib)
     assert wlk(tok=None) == bdm.EINVAL and "tokens" in err(lib)
     assert wlk(d=dims(block_len=0, total_rows=0)) == bdm.EINVAL and "block_len" in err(lib)
+
+
+def test_lattice_validates(lib):
+    d = dims()
+    big = 1 << 40
+    call = lambda **p: lib.dflash_lattice(
+        ctypes.byref(p.get("d", d)), p.get("tok", FAKE), p.get("un", FAKE), p.get("tables", FAKE),
+        p.get("gate", None), p.get("hidden", None), p.get("last", FAKE), p.get("offs", None), p.get("out", FAKE),
+        p.get("sc", FAKE), p.get("ws", FAKE), p.get("wsn", big), None)
+    assert call(tok=None) == bdm.EINVAL and "cand_tok" in err(lib)
+    assert call(un=None) == bdm.EINVAL and "unary" in err(lib)
+    assert call(tables=None) == bdm.EINVAL and "tables" in err(lib)
+    assert call(last=None) == bdm.EINVAL and "last_tok" in err(lib)
+    assert call(out=None) == bdm.EINVAL and "tokens" in err(lib)
+    assert call(sc=None) == bdm.EINVAL and "scores" in err(lib)
+    # the gate reads the hidden states
+    assert call(gate=FAKE) == bdm.EINVAL and "hidden" in err(lib)
+    assert call(d=dims(walk=5)) == bdm.EINVAL and "walk" in err(lib)
+    assert call(d=dims(total_rows=5)) == bdm.EINVAL and "row_offsets" in err(lib)
+    assert call(ws=None) == bdm.EWORKSPACE
+    assert call(wsn=16) == bdm.EWORKSPACE
+    assert call(ws=FAKE_ODD) == bdm.EINVAL and "aligned" in err(lib)
+    # no rows: nothing to launch
+    d0 = dims(num_requests=0, total_rows=0)
+    assert lib.dflash_lattice(ctypes.byref(d0), None, None, FAKE, None, None, None, None, None, None, FAKE,
+                              lib.dflash_workspace_bytes(ctypes.byref(d0)), None) == bdm.OK
+
+
+# ---------------------------------------------------------------- the binding's host checks
+# The C ABI trusts sizes, so the binding checks every tensor before any call.
+# CPU tensors suffice: shape and dtype checks come first, the device check last.
+
+torch = pytest.importorskip("torch")
+
+
+def _bf(*shape):
+    return torch.zeros(shape, dtype=torch.int16)
+
+
+def _step_args(M=6, H=64, Vd=1024, Vt=1024, r=16, R=2):
+    return dict(hidden=_bf(M, H), lm_head_w=_bf(Vd, H), tables=torch.zeros((2, Vt, r)),
+                last_tok=torch.zeros(R, dtype=torch.int64))
+
+
+@pytest.mark.parametrize("change,exc,word", [
+    (dict(lm_head_w=_bf(1024, 32)), ValueError, "lm_head"),                     # W narrower than H
+    (dict(tables=torch.zeros((1, 1024, 16))), ValueError, "tables"),            # one table instead of two
+    (dict(tables=torch.zeros((2, 1024, 16), dtype=torch.float64)), TypeError, "tables"),
+    (dict(hidden=torch.zeros((6, 64))), TypeError, "hidden"),                  # fp32 hidden
+    (dict(d2t=torch.zeros(1000, dtype=torch.int64)), ValueError, "d2t"),        # d2t of the wrong length
+    (dict(gate_w=torch.zeros(32)), ValueError, "gate_w"),                       # gate of the wrong length
+    (dict(last_tok=torch.zeros(2, dtype=torch.int32)), TypeError, "last_tok"),
+    (dict(row_offsets=torch.zeros(2, dtype=torch.int32)), ValueError, "row_offsets"),   # needs R + 1 entries
+    (dict(hidden=_bf(5, 64)), ValueError, "uniform blocks"),                    # 5 rows over 2 requests
+    (dict(block_len=4), ValueError, "block_len"),                               # uniform blocks of 3
+    (dict(out=(torch.zeros(5, dtype=torch.int64), torch.zeros(2))), ValueError, "tokens"),
+    (dict(out=(torch.zeros(6, dtype=torch.int64), torch.zeros(2, dtype=torch.float64))), TypeError, "scores"),
+    (dict(hidden=_bf(6, 64).t().contiguous().t()), ValueError, "contiguous"),
+    (dict(), ValueError, "GPU"),                                               # shapes fine: CPU tensors refused
+])
+def test_binding_rejects_mismatched_tensors(change, exc, word):
+    from block_draft_markov_amd import api
+    args = _step_args()
+    kw = dict(top_k=8)
+    for k, v in change.items():
+        (args if k in args else kw)[k] = v
+    with pytest.raises(exc, match=word):
+        api.draft_block(args.pop("hidden"), args.pop("lm_head_w"), args.pop("tables"), args.pop("last_tok"), **kw)
+
+
+def test_binding_ragged_offsets_checked_on_the_host():
+    from block_draft_markov_amd import api
+    a = _step_args(M=7)
+    off = torch.tensor([0, 5, 7], dtype=torch.int32)
+    with pytest.raises(ValueError, match="longer than block_len"):
+        api.draft_block(a["hidden"], a["lm_head_w"], a["tables"], a["last_tok"], top_k=8, row_offsets=off,
+                        block_len=3)
+    with pytest.raises(ValueError, match="non-decreasing"):
+        api.draft_block(a["hidden"], a["lm_head_w"], a["tables"], a["last_tok"], top_k=8,
+                        row_offsets=torch.tensor([0, 5, 4], dtype=torch.int32))
+    with pytest.raises(ValueError, match="exceeds"):
+        api.draft_block(a["hidden"], a["lm_head_w"], a["tables"], a["last_tok"], top_k=8,
+                        row_offsets=torch.tensor([0, 5, 9], dtype=torch.int32))
+    # well-formed offsets pass the host checks and stop only at the device check
+    with pytest.raises(ValueError, match="GPU"):
+        api.draft_block(a["hidden"], a["lm_head_w"], a["tables"], a["last_tok"], top_k=8, row_offsets=off)
+
+
+def test_binding_stage_entry_points_check_shapes():
+    from block_draft_markov_amd import api
+    tok = torch.zeros((6, 8), dtype=torch.int64)
+    un = torch.zeros((6, 8))
+    tables = torch.zeros((2, 100, 16))
+    last = torch.zeros(2, dtype=torch.int64)
+    with pytest.raises(ValueError, match="unary"):
+        api.lattice(tok, torch.zeros((6, 7)), tables, last)
+    with pytest.raises(ValueError, match="hidden is required"):
+        api.lattice(tok, un, tables, last, gate_w=torch.zeros(64))
+    with pytest.raises(ValueError, match="gate_w"):
+        api.lattice(tok, un, tables, last, gate_w=torch.zeros(32), hidden=_bf(6, 64))
+    with pytest.raises(ValueError, match="pair"):
+        api.walk(tok, un, torch.zeros((6, 8, 7)), 2)
+    with pytest.raises(ValueError, match="uniforms"):
+        api.walk_sampled(tok, un, torch.zeros((6, 8, 8)), 2, torch.zeros(5, dtype=torch.float64))
+    with pytest.raises(ValueError, match="lse"):
+        api.topk(torch.zeros((6, 1024)), torch.zeros(5), 8)
+    with pytest.raises(ValueError, match="d2t"):
+        api.topk(torch.zeros((6, 1024)), torch.zeros(6), 8, d2t=torch.zeros(1023, dtype=torch.int64))
+    with pytest.raises(ValueError, match="out"):
+        api.lm_head(_bf(6, 64), _bf(1024, 64), out=torch.zeros((6, 1000)))
+    with pytest.raises(ValueError, match="lm_head"):
+        api.draft_argmax(_bf(6, 64), _bf(1024, 48))
+    with pytest.raises(ValueError, match="values"):
+        api.draft_argmax(_bf(6, 64), _bf(1024, 64), out=(torch.zeros(6, dtype=torch.int64), torch.zeros(4)))
+    with pytest.raises(ValueError, match="tables"):
+        api.draft_dense(_bf(6, 64), _bf(1024, 64), torch.zeros((3, 1024, 16)), last)
+    with pytest.raises(TypeError, match="uniforms"):
+        api.draft_block_sampled(_bf(6, 64), _bf(1024, 64), torch.zeros((2, 1024, 16)), last,
+                                torch.zeros(6, dtype=torch.float32), top_k=8)

@@ -10,6 +10,13 @@ Bars (from the draft-step spec):
     values (rounded to fp32, the oracle re-walking those fp32 values in
     fp64); a case whose oracle runner-up margin is below 1e-6 * max(|S|, 1)
     is listed as an exemption; path scores within 1e-4 * max(|S|, 1);
+  * the whole step (GPU logits): tokens bit-exact and scores within 1e-4
+    for every request none of whose rows uses the Top-K boundary exemption
+    (a GPU candidate set that differs from the oracle's) and whose oracle
+    runner-up margin is at least 1e-5 * max(|S|, 1); an exempt request's
+    path must score within 1e-4 of the best path over the GPU's own
+    candidates (oracle, fp64).  Full-size workloads check every request and
+    allow at most a tenth of them to be exempt;
   * integer outputs (ids, target ids, slots) are compared exactly.
 """
 import numpy as np
@@ -18,7 +25,7 @@ import torch
 
 import draft_inputs as di
 from oracle import draft_step as O
-from tests.gpu_util import (check_topk_row, dev, dev_bf16, logits_tol, offsets_of, pack_pair, require_gpu, say,
+from tests.gpu_util import (check_topk_row, dev, dev_bf16, logits_tol, offsets_of, pack_pair, record, require_gpu, say,
                             upload)
 
 pytestmark = pytest.mark.gpu
@@ -324,7 +331,17 @@ def _staged(api_, d, inp, K, L, walk):
     return z, lse, idx, tok, un, tokens, scores, slots
 
 
-def _end_to_end(inp, sample_requests, walk="viterbi"):
+def _end_to_end(inp, sample_requests, walk="viterbi", name=None):
+    """The fused step against the oracle on the given requests.
+
+    A request is compared bit for bit (tokens, and the path score within
+    1e-4 * max(|S|, 1)) unless one of its rows uses the Top-K boundary
+    exemption (the GPU's candidate set differs from the oracle's), or the
+    oracle's runner-up margin is below 1e-5 * max(|S|, 1) (then an fp32 rounding
+    may pick the other path).  Exempt requests are re-walked by the oracle in
+    fp64 on the GPU's own candidates: the GPU path must score within 1e-4 of
+    that set's best.  Returns the counts.
+    """
     api_ = api()
     s = inp.shape
     R, M, K = len(inp.last_tok), inp.M, s.K
@@ -337,52 +354,74 @@ def _end_to_end(inp, sample_requests, walk="viterbi"):
                                         d2t=d["d2t"], gate_w=d["gate_w"], row_offsets=d["row_offsets"],
                                         block_len=L, walk=walk)
     z, lse, idx, tok, un, st_tokens, st_scores, st_slots = _staged(api_, d, inp, K, L, walk)
+    lat_tokens, lat_scores = api_.lattice(tok, un, d["tables"], d["last_tok"], gate_w=d["gate_w"],
+                                          hidden=d["hidden"], row_offsets=d["row_offsets"], block_len=L, walk=walk)
     torch.cuda.synchronize()
     tokens, scores = tokens.cpu().numpy(), scores.cpu().numpy()
     # deterministic, and the fused call equals the staged calls bit for bit
     assert np.array_equal(tokens, tokens2.cpu().numpy()) and np.array_equal(scores, scores2.cpu().numpy())
     assert np.array_equal(tokens, st_tokens.cpu().numpy())
     assert np.array_equal(scores, st_scores.cpu().numpy())
-    idx = idx.cpu().numpy()
+    assert np.array_equal(tokens, lat_tokens.cpu().numpy()) and np.array_equal(scores, lat_scores.cpu().numpy())
+    idx = idx.cpu().numpy().astype(np.int64)
     gtok = tok.cpu().numpy()
-    un = un.cpu().numpy()
     slots = st_slots.cpu().numpy()
-    counts = dict(rows_exact=0, rows_exempt=0, req_exact=0, req_exempt=0)
+    owalk = O.WALK_VITERBI if walk == "viterbi" else O.WALK_GREEDY
+    counts = dict(requests=0, req_exact=0, req_topk_exempt=0, req_margin_exempt=0, rows=0, rows_same=0,
+                  rows_reorder=0, rows_differs=0)
+    reqs = [r for r in sample_requests if off[r + 1] > off[r]]
     for req in sample_requests:
-        a, b = int(off[req]), int(off[req + 1])
-        if b == a:
+        if off[req + 1] == off[req]:
             assert scores[req] == 0.0
-            continue
+    if not reqs:
+        return counts
+    # the oracle's fp64 logits of every row of the sampled requests, in one product
+    rows_all = np.concatenate([np.arange(off[r], off[r + 1]) for r in reqs])
+    zo_all = O.logits(inp.hidden[rows_all], inp.lm_head)
+    zg_all = z.cpu().numpy()[rows_all].astype(np.float64)
+    base = 0
+    for req in reqs:
+        a, b = int(off[req]), int(off[req + 1])
+        n = b - a
         rows = np.arange(a, b)
-        zo = O.logits(inp.hidden[rows], inp.lm_head)
-        zg = z[a:b].cpu().numpy().astype(np.float64)
-        exempt_rows = 0
-        for i in range(b - a):
-            assert np.max(np.abs(zg[i] - zo[i])) <= logits_tol(zo[i])
-            kind = check_topk_row(idx[a + i], zo[i], K)
-            exempt_rows += kind == "exempt"
-        counts["rows_exact"] += (b - a) - exempt_rows
-        counts["rows_exempt"] += exempt_rows
-        sub = O.draft_from_logits(zo, K, inp.d2t, inp.tables, inp.hidden[rows], inp.gate_w, inp.last_tok[req:req + 1],
-                                  walk=O.WALK_VITERBI if walk == "viterbi" else O.WALK_GREEDY)
+        zo, zg = zo_all[base:base + n], zg_all[base:base + n]
+        base += n
+        counts["requests"] += 1
+        kinds = []
+        for i in range(n):
+            assert np.max(np.abs(zg[i] - zo[i])) <= logits_tol(zo[i]), f"request {req} row {i}: logits"
+            kinds.append(check_topk_row(idx[a + i], zo[i], K))
+        counts["rows"] += n
+        for k in ("same", "reorder", "differs"):
+            counts["rows_" + k] += kinds.count(k)
+        sub = O.draft_from_logits(zo, K, inp.d2t, inp.tables, inp.hidden[rows], inp.gate_w,
+                                  inp.last_tok[req:req + 1], walk=owalk)
         score, margin = sub.scores[0], sub.margins[0]
         scale = max(1.0, abs(score))
-        if exempt_rows == 0 and margin >= 1e-5 * scale:
-            assert np.array_equal(tokens[a:b], sub.tokens), f"request {req}: tokens differ"
-            assert abs(scores[req] - score) <= 1e-4 * scale
+        if "differs" not in kinds and margin >= 1e-5 * scale:
+            assert np.array_equal(tokens[a:b], sub.tokens), f"request {req}: tokens {tokens[a:b]} vs {sub.tokens}"
+            assert abs(scores[req] - score) <= 1e-4 * scale, f"request {req}: score {scores[req]} vs {score}"
             counts["req_exact"] += 1
-        else:
-            # the GPU's own candidate set, re-walked by the oracle in fp64: same best score within 1e-4
-            cand = O.Candidates(idx[a:b].astype(np.int64), gtok[a:b], np.take_along_axis(zo, idx[a:b].astype(np.int64), 1)
-                                - O.row_lse(zo)[:, None], None, O.row_lse(zo), None)
-            alt = O.walk_from_candidates(cand, inp.tables, inp.hidden[rows], inp.gate_w, inp.last_tok[req:req + 1],
-                                         walk=O.WALK_VITERBI if walk == "viterbi" else O.WALK_GREEDY)
-            gpu_path_score = O.path_score(cand.unary, alt.S[0], slots[a:b])
-            assert abs(gpu_path_score - alt.scores[0]) <= 1e-4 * max(1.0, abs(alt.scores[0]))
-            assert abs(scores[req] - alt.scores[0]) <= 1e-4 * max(1.0, abs(alt.scores[0]))
-            counts["req_exempt"] += 1
-    say(f"  {counts}")
+            continue
+        counts["req_topk_exempt" if "differs" in kinds else "req_margin_exempt"] += 1
+        # the GPU's own candidate set, re-walked by the oracle in fp64: same best score within 1e-4
+        lse_o = O.row_lse(zo)
+        cand = O.Candidates(idx[a:b], gtok[a:b], np.take_along_axis(zo, idx[a:b], 1) - lse_o[:, None], None, lse_o,
+                            None)
+        alt = O.walk_from_candidates(cand, inp.tables, inp.hidden[rows], inp.gate_w, inp.last_tok[req:req + 1],
+                                     walk=owalk)
+        gpu_path_score = O.path_score(cand.unary, alt.S[0], slots[a:b])
+        assert abs(gpu_path_score - alt.scores[0]) <= 1e-4 * max(1.0, abs(alt.scores[0]))
+        assert abs(scores[req] - alt.scores[0]) <= 1e-4 * max(1.0, abs(alt.scores[0]))
+    record(name or s.name, walk=walk, **counts)
     return counts
+
+
+def _assert_mostly_exact(c):
+    """Exemptions are rare (fp32 logits are ~1e-6 relative from the oracle's): at least one
+    request compared bit for bit, and at most a tenth of them (or one) exempt."""
+    assert c["req_exact"] >= 1, c
+    assert c["req_topk_exempt"] + c["req_margin_exempt"] <= max(1, c["requests"] // 10), c
 
 
 def test_end_to_end_tiny():
@@ -396,10 +435,11 @@ def test_end_to_end_tiny_stress_seeds(walk):
     for seed in range(2000, 2040):
         sh = di.custom_shape("tiny_stress", R=1, L=5, H=64, Vd=1024, K=8, r=16, table_std=0.5, seed=seed,
                              weight_seed=seed)
-        c = _end_to_end(di.make_inputs(sh), [0], walk)
+        c = _end_to_end(di.make_inputs(sh), [0], walk, name=f"tiny_stress_{seed}")
         exact += c["req_exact"]
-        assert c["req_exact"] + c["req_exempt"] == 1
+        assert c["req_exact"] + c["req_topk_exempt"] + c["req_margin_exempt"] == 1
     say(f"  {exact} of 40 requests outside every exemption, all bit-exact")
+    assert exact >= 36
 
 
 def test_end_to_end_gated_tiny_and_ragged():
@@ -425,20 +465,28 @@ def test_end_to_end_pruned_small_48():
 
 
 def test_end_to_end_qwen3_4b_single_request():
-    _end_to_end(di.make_inputs(di.SHAPES["qwen3_4b_1"]), [0])
+    c = _end_to_end(di.make_inputs(di.SHAPES["qwen3_4b_1"]), [0])
+    assert c["req_exact"] + c["req_topk_exempt"] + c["req_margin_exempt"] == 1
 
 
-def test_end_to_end_qwen3_4b_batch_sampled():
-    c = _end_to_end(di.make_inputs(di.SHAPES["qwen3_4b_32"]), [0, 13, 31])
-    assert c["req_exact"] + c["req_exempt"] == 3
+def test_end_to_end_qwen3_4b_batch_all_requests():
+    c = _end_to_end(di.make_inputs(di.SHAPES["qwen3_4b_32"]), range(32))
+    _assert_mostly_exact(c)
 
 
-def test_end_to_end_dflash2_27b_sampled():
-    _end_to_end(di.make_inputs(di.SHAPES["dflash2_27b"]), [0, 15])
+def test_end_to_end_qwen3_4b_batch_greedy_all_requests():
+    c = _end_to_end(di.make_inputs(di.SHAPES["qwen3_4b_32"]), range(32), walk="greedy")
+    _assert_mostly_exact(c)
 
 
-def test_end_to_end_pruned_ocr_sampled():
-    _end_to_end(di.make_inputs(di.SHAPES["pruned_ocr"]), [2, 9])
+def test_end_to_end_dflash2_27b_all_requests():
+    c = _end_to_end(di.make_inputs(di.SHAPES["dflash2_27b"]), range(16))
+    _assert_mostly_exact(c)
+
+
+def test_end_to_end_pruned_ocr_all_requests():
+    c = _end_to_end(di.make_inputs(di.SHAPES["pruned_ocr"]), range(16))
+    _assert_mostly_exact(c)
 
 
 def _zero_hidden(inp):

@@ -8,8 +8,9 @@ drawn slots and the recorded proposals must agree exactly; a draw whose
 U * total lies within 1e-12 * total of a running sum is exempt (counted,
 expected 0).  The whole step computes its own unary and pair values in fp32:
 there every position is re-drawn by the oracle from the GPU's candidates
-(fp64 unary and pair values) and the GPU's previous slot, and a draw with a
-relative gap below 1e-4 is exempt.
+(fp64 unary and pair values) and the GPU's previous slot, a draw with a
+relative gap below 5e-5 is exempt, and the exemptions are counted and
+bounded (see _sampled_end_to_end).
 """
 import numpy as np
 import pytest
@@ -17,7 +18,7 @@ import torch
 
 import draft_inputs as di
 from oracle import draft_step as O
-from tests.gpu_util import dev, dev_bf16, offsets_of, pack_pair, require_gpu, say, upload
+from tests.gpu_util import check_topk_row, dev, dev_bf16, offsets_of, pack_pair, record, require_gpu, say, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -109,7 +110,18 @@ def test_sampled_walk_fed_oracle_values_exact(name, lengths, K, ints, T):
     say(f"  exempt requests: {exempt}")
 
 
-def _sampled_end_to_end(inp, sample_requests, T, seed):
+def _sampled_end_to_end(inp, sample_requests, T, seed, name=None):
+    """The fused sampled step against the oracle on the given requests.
+
+    Every position is re-drawn by the oracle (fp64 unary and pair values) from
+    the GPU's candidates and the GPU's previous slot, with the same uniform.
+    The drawn slot must be the GPU's unless U * total lies within 5e-5 * total
+    of a running sum (fp32 rows are ~1e-6 relative from the oracle's; counted
+    as a gap exemption).  A position whose GPU candidates are not the oracle's
+    slots in the oracle's order (the Top-K boundary exemption, or ids closer
+    than the logit error swapped) is counted separately; its draw is still
+    checked on the GPU's candidates.
+    """
     A = api()
     R, M, K = len(inp.last_tok), inp.M, inp.shape.K
     off = offsets_of(R, M, inp.row_offsets)
@@ -133,32 +145,47 @@ def _sampled_end_to_end(inp, sample_requests, T, seed):
     assert np.array_equal(tokens, st_tokens.cpu().numpy()) and np.array_equal(scores, st_scores.cpu().numpy())
     assert np.array_equal(q, st_q.cpu().numpy())
     idx, gtok, slots = idx.cpu().numpy().astype(np.int64), tok.cpu().numpy(), st_slots.cpu().numpy()
-    counts = dict(exact=0, exempt=0)
+    counts = dict(positions=0, exact=0, gap_exempt=0, topk_exempt=0)
+    reqs = [r for r in sample_requests if off[r + 1] > off[r]]
     for req in sample_requests:
-        a, b = int(off[req]), int(off[req + 1])
-        if b == a:
+        if off[req + 1] == off[req]:
             assert scores[req] == 0.0
-            continue
+    if not reqs:
+        return counts
+    rows_all = np.concatenate([np.arange(off[r], off[r + 1]) for r in reqs])
+    zo_all = O.logits(inp.hidden[rows_all], inp.lm_head)
+    base = 0
+    for req in reqs:
+        a, b = int(off[req]), int(off[req + 1])
         rows = np.arange(a, b)
-        zo = O.logits(inp.hidden[rows], inp.lm_head)
+        zo = zo_all[base:base + (b - a)]
+        base += b - a
+        kinds = [check_topk_row(idx[a + i], zo[i], K) for i in range(b - a)]
         lse = O.row_lse(zo)
         u_o = np.take_along_axis(zo, idx[a:b], 1) - lse[:, None]        # fp64 unary of the GPU's slots
         h = O.bf16_to_f64(inp.hidden[rows])
         S_o = O.lattice_scores(gtok[a:b], inp.tables, h, inp.gate_w, int(inp.last_tok[req]))
         for p in range(b - a):
+            counts["positions"] += 1
             prev = 0 if p == 0 else int(slots[a + p - 1])
             row = S_o[p][prev:prev + 1] if p > 0 else S_o[0][:1]
             sw = O.sampled(u_o[p:p + 1], [row], U[a + p:a + p + 1], temperature=T)
-            if sw.gaps[0] < 1e-4:
-                counts["exempt"] += 1
+            if kinds[p] != "same":
+                counts["topk_exempt"] += 1
+            if sw.gaps[0] < 5e-5:
+                counts["gap_exempt"] += 1
             else:
                 assert slots[a + p] == sw.path[0], f"request {req} position {p}: slot {slots[a + p]} vs {sw.path[0]}"
-                counts["exact"] += 1
-            assert np.max(np.abs(q[a + p] - sw.q[0])) <= 1e-4, f"request {req} position {p}: proposal"
+                counts["exact"] += kinds[p] == "same"
+            assert np.max(np.abs(q[a + p] - sw.q[0])) <= 1e-5, f"request {req} position {p}: proposal"
             assert tokens[a + p] == gtok[a + p][slots[a + p]]
         gpu_score = O.path_score(u_o, S_o, slots[a:b])
         assert abs(scores[req] - gpu_score) <= 1e-4 * max(1.0, abs(gpu_score))
-    say(f"  {counts}")
+    record(name or inp.shape.name, sampled=True, temperature=T, **counts)
+    n = counts["positions"]
+    assert counts["exact"] >= 1, counts
+    assert counts["gap_exempt"] <= max(3, n // 25), counts
+    assert counts["topk_exempt"] <= max(1, n // 10), counts
     return counts
 
 
@@ -186,13 +213,19 @@ def test_sampled_end_to_end_pruned_48():
     _sampled_end_to_end(di.make_inputs(sh), range(3), T=1.0, seed=6)
 
 
-def test_sampled_end_to_end_qwen3_4b_batch_sampled_requests():
-    """The Qwen3-4B batch (32 requests x 7 rows), three requests checked against the oracle."""
+def test_sampled_end_to_end_qwen3_4b_batch_all_requests():
+    """The Qwen3-4B batch (32 requests x 7 rows), every request against the oracle."""
     inp = di.make_inputs(di.SHAPES["qwen3_4b_32"])
-    _sampled_end_to_end(inp, [0, 13, 31], T=1.0, seed=7)
+    _sampled_end_to_end(inp, range(32), T=1.0, seed=7)
 
 
-def test_sampled_end_to_end_dflash2_27b_sampled_requests():
-    """The gated 27B shape (16 requests x 15 rows, V 248100, H 5120), two requests against the oracle."""
+def test_sampled_end_to_end_dflash2_27b_all_requests():
+    """The gated 27B shape (16 requests x 15 rows, V 248100, H 5120), every request against the oracle."""
     inp = di.make_inputs(di.SHAPES["dflash2_27b"])
-    _sampled_end_to_end(inp, [0, 15], T=1.0, seed=8)
+    _sampled_end_to_end(inp, range(16), T=1.0, seed=8)
+
+
+def test_sampled_end_to_end_pruned_ocr_all_requests():
+    """The pruned vocabulary (16 requests x 15 rows, 114688 -> 248100), every request against the oracle."""
+    inp = di.make_inputs(di.SHAPES["pruned_ocr"])
+    _sampled_end_to_end(inp, range(16), T=0.9, seed=9)
