@@ -93,6 +93,13 @@ class Timer:
             self.flush_buf = self.torch.zeros(1 << 30, dtype=self.torch.uint8, device="cuda")
         self.flush_buf.add_(1)
 
+    def prime(self, cycles):
+        """Queue a bounded GPU spin so that the host can queue work ahead of the GPU."""
+        try:
+            self.torch.cuda._sleep(int(cycles))
+        except (AttributeError, RuntimeError):
+            pass
+
     def region(self, fn, n, warm):
         """Mean ms per call of n calls between two events, after `warm` untimed calls."""
         torch = self.torch
@@ -118,10 +125,7 @@ class Timer:
             fn()
         torch.cuda.synchronize()
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
-        try:
-            torch.cuda._sleep(int(n * 100_000))
-        except (AttributeError, RuntimeError):
-            pass
+        self.prime(n * 100_000)
         for a, b in ev:
             if cold:
                 self.flush()
@@ -274,16 +278,18 @@ def main():
     shape = w.shape
     R, L, M, H, Vd, Vt, K, r = shape.R, shape.L, shape.M, shape.H, shape.Vd, shape.Vt, shape.K, shape.r
 
-    # ---- the timed region: exactly --steps whole steps
-    log(f"warmup {args.warmup}, timing {args.steps} steps")
-    ms = timer.region(w.step, args.steps, args.warmup)
-    blocks_per_s = R / (ms / 1e3)
-    rows_per_s = M / (ms / 1e3)
-    log(f"{ms * 1e3:.1f} us/step -> {blocks_per_s:.0f} blocks/s, {rows_per_s:.0f} rows/s")
-
     # ---- per-iteration distributions, warm and cold
     main_entry = workload_entry(w, timer, args)
     log(f"per-iteration: warm {main_entry['step_warm']}, cold {main_entry['step_cold']}")
+    # host time to enqueue one step (binding + C ABI + four launches), GPU not awaited
+    torch.cuda.synchronize()
+    timer.prime(50 * 2_000_000)
+    t0 = time.perf_counter()
+    for _ in range(50):
+        w.step()
+    host_us = (time.perf_counter() - t0) / 50 * 1e6
+    torch.cuda.synchronize()
+    log(f"host enqueue time per step: {host_us:.1f} us")
 
     # ---- every stage entry point alone (per-iteration events, warm unless stated)
     zbuf = torch.empty((M, api.logits_stride(Vd)), dtype=torch.float32, device="cuda")
@@ -328,6 +334,14 @@ def main():
               "bf16_mm_tflops": round(2 * 8192 ** 3 / (mm["median_us"] * 1e-6) / 1e12, 1),
               "probes": "torch fp32 sum over 2 GiB (cold), torch.mm 8192^3 bf16"}
     log(f"attainable: {attain}")
+
+    # ---- the timed region: exactly --steps whole steps after --warmup untimed ones (run after
+    # the measurements above, so that the GPU is at its working clocks)
+    log(f"warmup {args.warmup}, timing {args.steps} steps")
+    ms = timer.region(w.step, args.steps, args.warmup)
+    blocks_per_s = R / (ms / 1e3)
+    rows_per_s = M / (ms / 1e3)
+    log(f"{ms * 1e3:.1f} us/step -> {blocks_per_s:.0f} blocks/s, {rows_per_s:.0f} rows/s")
 
     # ---- roofline of the dominant kernel (the lm_head GEMM with its LSE epilogue), launched alone
     b = step_bytes(shape)
@@ -377,6 +391,7 @@ def main():
                      "mfma_tflops": round(k1_tflops, 1), "mfma_peak_tflops": BF16_MFMA_PEAK_TFLOPS,
                      "mfma_frac": round(k1_tflops / BF16_MFMA_PEAK_TFLOPS, 4)},
         "timing": {"warm": main_entry["step_warm"], "cold": main_entry["step_cold"],
+                   "host_enqueue_us_per_step": round(host_us, 1),
                    "cold_flush": "1 GiB read-modify-write before every iteration, outside the events"},
         "step_roofline": main_entry["roofline"],
         "standalone_topk_pass": {"achieved_gbs": round(k2_gbs, 1), "frac": round(k2_gbs / HBM_PEAK_GBS, 4),
