@@ -13,6 +13,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdflash_d
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, -1, -2, -3, -4
 WALK_VITERBI, WALK_GREEDY = 0, 1
 MAX_TOP_K, MAX_BLOCK_LEN = 64, 100
+LATTICE_NOALLOC_MAX_BYTES = 16 << 20
 
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
@@ -48,6 +49,7 @@ SIGNATURES = {
     "dflash_pair_scores": (ctypes.c_int, [_PD, _P, _P, _P, _P, _P, _P, _P, _P]),
     "dflash_walk": (ctypes.c_int, [_PD, _P, _P, _P, _P, _P, _P, _P, _P]),
     "dflash_lattice": (ctypes.c_int, [_PD, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "dflash_lattice_noalloc": (ctypes.c_int, [_PD, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "dflash_draft_argmax": (ctypes.c_int, [_PD, _P, _P, _P, ctypes.c_float, ctypes.c_float, _P, _P, _P, _SZ, _P]),
     "dflash_draft_dense": (ctypes.c_int, [_PD, _P, _P, _P, _P, _P, _P, ctypes.c_float, ctypes.c_float, _P, _P, _P,
                                           _SZ, _P]),

@@ -21,7 +21,7 @@ from ._lib import (DFlashError, Dims, MAX_BLOCK_LEN, WALK_GREEDY, WALK_VITERBI, 
 
 __all__ = ["Dims", "DFlashError", "make_dims", "workspace_bytes", "logits_stride", "draft_block",
            "draft_block_sampled", "draft_argmax", "draft_dense", "lm_head", "row_lse", "topk", "pair_scores",
-           "walk", "walk_sampled", "lattice", "check_d2t", "Workspace"]
+           "walk", "walk_sampled", "lattice", "lattice_noalloc", "check_d2t", "Workspace"]
 
 _WALKS = {"viterbi": WALK_VITERBI, "greedy": WALK_GREEDY, WALK_VITERBI: WALK_VITERBI, WALK_GREEDY: WALK_GREEDY}
 
@@ -468,6 +468,38 @@ def lattice(cand_tok: torch.Tensor, unary: torch.Tensor, tables: torch.Tensor, l
     check(load().dflash_lattice(ctypes.byref(d), _ptr(cand_tok), _ptr(unary), _ptr(tables), _ptr(gate_w),
                                 _ptr(hidden), _ptr(last_tok), _ptr(row_offsets), _ptr(tokens), _ptr(scores),
                                 wsp, wsn, _stream(dev)))
+    return tokens, scores
+
+
+def lattice_noalloc(cand_tok: torch.Tensor, unary: torch.Tensor, tables: torch.Tensor, last_tok: torch.Tensor, *,
+                    gate_w: Optional[torch.Tensor] = None, hidden: Optional[torch.Tensor] = None,
+                    row_offsets: Optional[torch.Tensor] = None, block_len: Optional[int] = None, walk="viterbi",
+                    out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None):
+    """lattice() without a workspace: S lives in the library's static device scratch
+    (at most LATTICE_NOALLOC_MAX_BYTES per GPU; overlapping calls on one GPU race).
+    The outputs are allocated here unless `out` is given; the C call allocates nothing."""
+    M, K = _cand_args(cand_tok, unary)
+    if unary is None:
+        raise ValueError("unary is required")
+    _arg(tables, "tables", _F32, (2, None, None))
+    Vt, r = tables.shape[1], tables.shape[2]
+    _arg(last_tok, "last_tok", _I64, (None,))
+    R = last_tok.shape[0]
+    _arg(row_offsets, "row_offsets", _I32, (R + 1,), optional=True)
+    _arg(hidden, "hidden", _BF16, (M, None), optional=gate_w is None)
+    H = hidden.shape[1] if hidden is not None else 8
+    _arg(gate_w, "gate_w", _F32, (H,), optional=True)
+    dev = cand_tok.device
+    tokens, scores = _outs(out, dev, [("tokens", _I64, (M,), False), ("scores", _F32, (R,), False)])
+    L = _block_len(R, M, row_offsets, block_len)
+    _check_block_len(L)
+    _on_device(dev, unary=unary, tables=tables, last_tok=last_tok, gate_w=gate_w, hidden=hidden,
+               row_offsets=row_offsets)
+    d = make_dims(R=R, L=L, M=M, H=H, Vd=max(K, 1), Vt=Vt, K=K, r=r, walk=walk)
+    with torch.cuda.device(dev):
+        check(load().dflash_lattice_noalloc(ctypes.byref(d), _ptr(cand_tok), _ptr(unary), _ptr(tables),
+                                            _ptr(gate_w), _ptr(hidden), _ptr(last_tok), _ptr(row_offsets),
+                                            _ptr(tokens), _ptr(scores), _stream(dev)))
     return tokens, scores
 
 

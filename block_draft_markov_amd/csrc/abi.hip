@@ -13,6 +13,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <vector>
 
 namespace {
@@ -182,6 +183,67 @@ int check_sampling(const dflash_dims* d, const double* uniforms, float temperatu
     if (!(temperature > 0.f) || !std::isfinite(temperature))
         return fail(DFLASH_EINVAL, "temperature = %g must be finite and positive", (double)temperature);
     return need(uniforms, d->total_rows, "uniforms");
+}
+
+// ---------------------------------------------------------------- static scratch
+// The scratch of dflash_lattice_noalloc: the S lattice of the call, in a
+// device array of the library (one copy per GPU, alive until the process
+// ends), so that the call allocates nothing.  Host code never passes the
+// array's name to a kernel: it takes the device address of the copy on the
+// current GPU from hipGetSymbolAddress, once per device, and uses that.
+constexpr size_t kScratchBytes = DFLASH_LATTICE_NOALLOC_MAX_BYTES;
+static_assert(kScratchBytes % 256 == 0, "scratch size");
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Address of the current device's copy of `scratch` (looked up on the first call per device).
+int scratch_address(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(DFLASH_EINVAL, "device %d beyond the %d supported", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if ((e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) != hipSuccess)
+            return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!p) return fail(DFLASH_EHIP, "hipGetSymbolAddress(scratch) returned NULL");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return DFLASH_OK;
+}
+
+// Host-side checks shared by dflash_lattice and dflash_lattice_noalloc.
+int check_lattice(const dflash_dims* d, const int64_t* cand_tok, const float* unary, const float* tables,
+                  const float* gate_w, const uint16_t* hidden, const int64_t* last_tok, const int32_t* row_offsets,
+                  const int64_t* tokens, const float* scores) {
+    int rc;
+    if ((rc = check_dims(d)) || (rc = check_rows(d, row_offsets))) return rc;
+    const int64_t M = d->total_rows, R = d->num_requests;
+    if ((rc = need(cand_tok, M, "cand_tok")) || (rc = need(unary, M, "unary")) || (rc = need(tables, 1, "tables")) ||
+        (rc = need(last_tok, R, "last_tok")) || (rc = need(tokens, M, "tokens")) || (rc = need(scores, R, "scores")))
+        return rc;
+    if (gate_w && (rc = need(hidden, M, "hidden (read by the gate)"))) return rc;
+    return DFLASH_OK;
+}
+
+// Pair scores into `pair`, then the walk from them.
+int launch_lattice(const dflash_dims* d, const int64_t* cand_tok, const float* unary, const float* tables,
+                   const float* gate_w, const uint16_t* hidden, const int64_t* last_tok, const int32_t* row_offsets,
+                   int64_t* tokens, float* scores, float* pair, hipStream_t s) {
+    hipError_t e;
+    if ((e = dflash::launch_pair_scores(cand_tok, tables, gate_w, hidden, last_tok, row_offsets, d->num_requests,
+                                        d->block_len, d->total_rows, d->hidden, d->target_vocab, d->top_k, d->rank,
+                                        pair, s)) != hipSuccess)
+        return hip_fail(e, "pair-score launch");
+    if ((e = dflash::launch_walk(cand_tok, unary, pair, row_offsets, d->num_requests, d->block_len, d->total_rows,
+                                 d->top_k, d->walk, tokens, scores, nullptr, s)) != hipSuccess)
+        return hip_fail(e, "walk launch");
+    return DFLASH_OK;
 }
 
 }  // namespace
@@ -401,24 +463,33 @@ int dflash_lattice(const dflash_dims* d, const int64_t* cand_tok, const float* u
                    const float* gate_w, const uint16_t* hidden, const int64_t* last_tok, const int32_t* row_offsets,
                    int64_t* tokens, float* scores, void* ws, size_t ws_bytes, void* stream) {
     int rc;
-    if ((rc = check_dims(d)) || (rc = check_rows(d, row_offsets))) return rc;
-    const int64_t M = d->total_rows, R = d->num_requests;
-    if ((rc = need(cand_tok, M, "cand_tok")) || (rc = need(unary, M, "unary")) || (rc = need(tables, 1, "tables")) ||
-        (rc = need(last_tok, R, "last_tok")) || (rc = need(tokens, M, "tokens")) || (rc = need(scores, R, "scores")))
+    if ((rc = check_lattice(d, cand_tok, unary, tables, gate_w, hidden, last_tok, row_offsets, tokens, scores)))
         return rc;
-    if (gate_w && (rc = need(hidden, M, "hidden (read by the gate)"))) return rc;
     Layout l;
     if ((rc = check_ws(d, ws, ws_bytes, l))) return rc;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e;
-    float* pair = at<float>(ws, l.pair);
-    if ((e = dflash::launch_pair_scores(cand_tok, tables, gate_w, hidden, last_tok, row_offsets, d->num_requests,
-                                        d->block_len, d->total_rows, d->hidden, d->target_vocab, d->top_k, d->rank,
-                                        pair, s)) != hipSuccess)
-        return hip_fail(e, "pair-score launch");
-    if ((e = dflash::launch_walk(cand_tok, unary, pair, row_offsets, d->num_requests, d->block_len, d->total_rows,
-                                 d->top_k, d->walk, tokens, scores, nullptr, s)) != hipSuccess)
-        return hip_fail(e, "walk launch");
+    if ((rc = launch_lattice(d, cand_tok, unary, tables, gate_w, hidden, last_tok, row_offsets, tokens, scores,
+                             at<float>(ws, l.pair), static_cast<hipStream_t>(stream))))
+        return rc;
+    return ok();
+}
+
+int dflash_lattice_noalloc(const dflash_dims* d, const int64_t* cand_tok, const float* unary, const float* tables,
+                           const float* gate_w, const uint16_t* hidden, const int64_t* last_tok,
+                           const int32_t* row_offsets, int64_t* tokens, float* scores, void* stream) {
+    int rc;
+    if ((rc = check_lattice(d, cand_tok, unary, tables, gate_w, hidden, last_tok, row_offsets, tokens, scores)))
+        return rc;
+    const size_t need_bytes = (size_t)d->total_rows * (size_t)d->top_k * (size_t)d->top_k * sizeof(float);
+    if (need_bytes > kScratchBytes)
+        return fail(DFLASH_EINVAL, "total_rows * top_k^2 * 4 = %zu bytes exceeds the %zu-byte static scratch of "
+                    "dflash_lattice_noalloc", need_bytes, kScratchBytes);
+    if (d->num_requests == 0) return ok();   // nothing to launch
+    void* sp = nullptr;
+    if ((rc = scratch_address(&sp))) return rc;
+    // every S entry the walk reads is written by the pair-score kernel first: nothing to clear
+    if ((rc = launch_lattice(d, cand_tok, unary, tables, gate_w, hidden, last_tok, row_offsets, tokens, scores,
+                             static_cast<float*>(sp), static_cast<hipStream_t>(stream))))
+        return rc;
     return ok();
 }
 

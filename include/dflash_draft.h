@@ -200,6 +200,25 @@ int dflash_lattice(const dflash_dims* dims, const int64_t* cand_tok, const float
                    const int32_t* row_offsets, int64_t* tokens, float* scores,
                    void* workspace, size_t workspace_bytes, void* stream);
 
+/* dflash_lattice for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, kernels and results as dflash_lattice, without the
+ * workspace: S lives in a static device array of the library,
+ * DFLASH_LATTICE_NOALLOC_MAX_BYTES bytes per GPU, held until the process ends.
+ * The call allocates nothing (no hipMalloc, no allocating library routine).
+ *   Limit: total_rows * top_k^2 * 4 <= DFLASH_LATTICE_NOALLOC_MAX_BYTES
+ *          (1024 rows at K = 64); larger calls return DFLASH_EINVAL.
+ *   The array of a GPU is shared by every call on it and keeps the last
+ *   call's contents (every entry a call reads is written by that call first):
+ *   calls that overlap on one GPU (other streams, other threads) race and must
+ *   be serialised by the caller.  The GPU is the device current on the calling
+ *   thread; the stream and every buffer must belong to it. */
+#define DFLASH_LATTICE_NOALLOC_MAX_BYTES (16u << 20)
+int dflash_lattice_noalloc(const dflash_dims* dims, const int64_t* cand_tok, const float* unary,
+                           const float* tables, const float* gate_w, const uint16_t* hidden,
+                           const int64_t* last_tok, const int32_t* row_offsets,
+                           int64_t* tokens, float* scores, void* stream);
+
 /* Sampled drafting (openvino.genai page "Add DSpark and DFlash v2 drafts and
  * sampled drafting ...", commit "DFlash-2 Markov head / BlockRowSource": a
  * sampled request walks the lattice with the request's draft RNG; the

@@ -44,7 +44,7 @@ def err(lib):
 
 def test_every_declared_symbol_is_exported(lib):
     names = header_functions()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     for n in names:
         assert hasattr(lib, n), f"{n} declared in include/ but not exported"
     assert set(names) == set(bdm.SIGNATURES), "binding and header disagree"
@@ -313,6 +313,26 @@ def test_lattice_validates(lib):
     d0 = dims(num_requests=0, total_rows=0)
     assert lib.dflash_lattice(ctypes.byref(d0), None, None, FAKE, None, None, None, None, None, None, FAKE,
                               lib.dflash_workspace_bytes(ctypes.byref(d0)), None) == bdm.OK
+
+
+def test_lattice_noalloc_validates_before_touching_the_gpu(lib):
+    from block_draft_markov_amd._lib import LATTICE_NOALLOC_MAX_BYTES
+    call = lambda d, **p: lib.dflash_lattice_noalloc(
+        ctypes.byref(d), p.get("tok", FAKE), p.get("un", FAKE), p.get("tables", FAKE), p.get("gate", None),
+        p.get("hidden", None), p.get("last", FAKE), None, p.get("out", FAKE), p.get("sc", FAKE), None)
+    # more rows than the static scratch holds at K = 64: rejected with the limit in the message
+    rows = LATTICE_NOALLOC_MAX_BYTES // (64 * 64 * 4) + 1
+    big = dims(num_requests=rows, block_len=1, total_rows=rows, draft_vocab=64, target_vocab=100, top_k=64)
+    assert call(big) == bdm.EINVAL and "static scratch" in err(lib)
+    fits = dims(num_requests=rows - 1, block_len=1, total_rows=rows - 1, draft_vocab=64, target_vocab=100, top_k=64)
+    assert call(fits, tok=None) == bdm.EINVAL and "cand_tok" in err(lib)
+    assert call(dims(), gate=FAKE) == bdm.EINVAL and "hidden" in err(lib)
+    assert call(dims(walk=4)) == bdm.EINVAL and "walk" in err(lib)
+    # no requests: nothing to launch, no device touched
+    assert lib.dflash_lattice_noalloc(ctypes.byref(dims(num_requests=0, total_rows=0)), None, None, FAKE, None,
+                                      None, None, None, None, None, None) == bdm.OK
+    h = open(os.path.join(ROOT, "include", "dflash_draft.h")).read()
+    assert f"DFLASH_LATTICE_NOALLOC_MAX_BYTES (16u << 20)" in h and LATTICE_NOALLOC_MAX_BYTES == 16 << 20
 
 
 # ---------------------------------------------------------------- the binding's host checks
