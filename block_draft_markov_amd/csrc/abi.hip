@@ -137,11 +137,14 @@ T* at(void* ws, size_t off) {
     return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
 }
 
-// Parts 1-3 of a whole step (validation, then lm_head, Top-K and pair scores);
-// the caller launches the walk.
-int lattice_stages(const dflash_dims* d, const uint16_t* hidden, const uint16_t* lm_head, const int64_t* d2t,
-                   const float* tables, const float* gate_w, const int64_t* last_tok, const int32_t* row_offsets,
-                   int64_t* tokens, float* scores, void* ws, size_t ws_bytes, void* stream, Layout& l) {
+constexpr int kSampled = 2;   // walk argument of whole_step: the sampled walk
+
+// The whole step: validation, then the lm_head kernel, the Top-K from its tile
+// maxima, the pair scores and the walk, in stream order.
+int whole_step(const dflash_dims* d, const uint16_t* hidden, const uint16_t* lm_head, const int64_t* d2t,
+               const float* tables, const float* gate_w, const int64_t* last_tok, const int32_t* row_offsets,
+               int walk, const double* uniforms, float temperature, int64_t* tokens, float* scores, double* q,
+               void* ws, size_t ws_bytes, void* stream) {
     int rc;
     if ((rc = check_dims(d)) || (rc = check_rows(d, row_offsets))) return rc;
     const int64_t M = d->total_rows, R = d->num_requests;
@@ -157,25 +160,37 @@ int lattice_stages(const dflash_dims* d, const uint16_t* hidden, const uint16_t*
                                          "not supported");
     if (!aligned(hidden, 16) || !aligned(lm_head, 16))
         return fail(DFLASH_EINVAL, "hidden and lm_head must be 16-byte aligned");
+    Layout l;
     if ((rc = check_ws(d, ws, ws_bytes, l))) return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
     float* logits = at<float>(ws, l.logits);
     float2* part = at<float2>(ws, l.part);
-    float* tmax = l.ldt ? at<float>(ws, l.tmax) : nullptr;
+    float* tmax = at<float>(ws, l.tmax);
+    // the lm_head kernel stores the tile maxima (there are some whenever there are rows)
     if ((e = dflash::launch_lmhead(hidden, lm_head, logits, l.ldz, part, tmax, l.ldt, d->total_rows, d->hidden,
                                    d->draft_vocab, s)) != hipSuccess)
         return hip_fail(e, "lm_head launch");
-    // the lm_head kernel stored the tile maxima (there are some whenever there are rows)
+    int32_t* cidx = at<int32_t>(ws, l.cidx);
+    int64_t* ctok = at<int64_t>(ws, l.ctok);
+    float* unary = at<float>(ws, l.unary);
+    float* pair = at<float>(ws, l.pair);
     if ((e = dflash::launch_topk_tiles(logits, l.ldz, tmax, l.ldt, nullptr, part, l.nparts, d2t, d->total_rows,
-                                       d->draft_vocab, d->top_k, at<int32_t>(ws, l.cidx), at<int64_t>(ws, l.ctok),
-                                       at<float>(ws, l.unary), s)) != hipSuccess)
+                                       d->draft_vocab, d->top_k, cidx, ctok, unary, s)) != hipSuccess)
         return hip_fail(e, "top-k launch");
-    if ((e = dflash::launch_pair_scores(at<int64_t>(ws, l.ctok), tables, gate_w, hidden, last_tok, row_offsets,
-                                        d->num_requests, d->block_len, d->total_rows, d->hidden, d->target_vocab,
-                                        d->top_k, d->rank, at<float>(ws, l.pair), s)) != hipSuccess)
+    if ((e = dflash::launch_pair_scores(ctok, tables, gate_w, hidden, last_tok, row_offsets, d->num_requests,
+                                        d->block_len, d->total_rows, d->hidden, d->target_vocab, d->top_k, d->rank,
+                                        pair, s)) != hipSuccess)
         return hip_fail(e, "pair-score launch");
-    return DFLASH_OK;
+    if (walk == kSampled)
+        e = dflash::launch_walk_sampled(ctok, unary, pair, row_offsets, d->num_requests, d->block_len, d->total_rows,
+                                        d->top_k, uniforms, temperature, tokens, scores, nullptr, q, s);
+    else
+        e = dflash::launch_walk(ctok, unary, pair, row_offsets, d->num_requests, d->block_len, d->total_rows,
+                                d->top_k, walk, tokens, scores, nullptr, s);
+    if (e != hipSuccess)
+        return hip_fail(e, "walk launch");
+    return ok();
 }
 
 // The sampled walk's own arguments: a uniform per row, a finite positive temperature.
@@ -262,17 +277,9 @@ int dflash_draft_block(const dflash_dims* d, const uint16_t* hidden, const uint1
                        const float* tables, const float* gate_w, const int64_t* last_tok,
                        const int32_t* row_offsets, int64_t* tokens, float* scores, void* ws, size_t ws_bytes,
                        void* stream) {
-    int rc;
-    Layout l;
-    if ((rc = lattice_stages(d, hidden, lm_head, d2t, tables, gate_w, last_tok, row_offsets, tokens, scores, ws,
-                             ws_bytes, stream, l)))
-        return rc;
-    hipError_t e;
-    if ((e = dflash::launch_walk(at<int64_t>(ws, l.ctok), at<float>(ws, l.unary), at<float>(ws, l.pair),
-                                 row_offsets, d->num_requests, d->block_len, d->total_rows, d->top_k, d->walk,
-                                 tokens, scores, nullptr, static_cast<hipStream_t>(stream))) != hipSuccess)
-        return hip_fail(e, "walk launch");
-    return ok();
+    if (!d) return fail(DFLASH_EINVAL, "dims is NULL");
+    return whole_step(d, hidden, lm_head, d2t, tables, gate_w, last_tok, row_offsets, d->walk, nullptr, 1.f, tokens,
+                      scores, nullptr, ws, ws_bytes, stream);
 }
 
 int dflash_draft_block_sampled(const dflash_dims* d, const uint16_t* hidden, const uint16_t* lm_head,
@@ -282,17 +289,8 @@ int dflash_draft_block_sampled(const dflash_dims* d, const uint16_t* hidden, con
                                size_t ws_bytes, void* stream) {
     int rc;
     if ((rc = check_dims(d)) || (rc = check_sampling(d, uniforms, temperature))) return rc;
-    Layout l;
-    if ((rc = lattice_stages(d, hidden, lm_head, d2t, tables, gate_w, last_tok, row_offsets, tokens, scores, ws,
-                             ws_bytes, stream, l)))
-        return rc;
-    hipError_t e;
-    if ((e = dflash::launch_walk_sampled(at<int64_t>(ws, l.ctok), at<float>(ws, l.unary), at<float>(ws, l.pair),
-                                         row_offsets, d->num_requests, d->block_len, d->total_rows, d->top_k,
-                                         uniforms, temperature, tokens, scores, nullptr, q,
-                                         static_cast<hipStream_t>(stream))) != hipSuccess)
-        return hip_fail(e, "sampled walk launch");
-    return ok();
+    return whole_step(d, hidden, lm_head, d2t, tables, gate_w, last_tok, row_offsets, kSampled,
+                      uniforms, temperature, tokens, scores, q, ws, ws_bytes, stream);
 }
 
 int dflash_draft_argmax(const dflash_dims* d, const uint16_t* hidden, const uint16_t* lm_head, const int64_t* d2t,

@@ -1,378 +1,28 @@
-// Parts 3 and 4 of the draft step: the Markov-head candidate scorer over the
-// packed Top-K lattice and the walk through it.
-//
-// Scorer (optimum-intel page "Export DFlash v2 and DSpark drafts ...", What
-// does this PR do?: the Top-K lattice of the DSpark head, with transitions
-// gated by the draft hidden states for DFlash v2; openvino.genai page "Add
-// DSpark and DFlash v2 drafts ...", commit "DFlash-2 Markov head /
-// BlockRowSource": one run over the packed block rows of all requests):
-//   S_p[j][k] = g_p * <A[t_{p-1}[j]], B[t_p[k]]>,  S_0[0][k] = g_0 * <A[last], B[t_0[k]]>,
-//   g_p = sigmoid(w . h_p) when gated, else 1.
-// One workgroup per (position, request).  The K rows of A and of B it needs
-// are gathered whole (up to 256 rank elements at a time), every load in flight
-// at once, into LDS rows of 260 floats (the 32 rows a wave reads fall in
-// distinct banks); each of the four waves computes one 32 x 32 quadrant of S
-// with fp32 MFMAs.
-//
-// Walk (same commit: the greedy walk takes the best candidate after the token
-// before; the max-score walk is its Viterbi form): one 256-thread workgroup per
-// request stages up to eight positions of S and u in LDS at a time.  Viterbi:
-// thread (k, q) takes the best delta(j) + S[j][k] over j in its quarter q of
-// the slots (ascending, strict >), and the quarters are combined in order, so
-// the lowest j wins a tie; back-pointers stay in LDS.  Greedy: one wave, an
-// argmax per position (DPP max reduction, lowest lane of a ballot).  Sampled
-// (same commit: a sampled request walks the lattice with its draft RNG; the
-// sampled-drafting commits: float weights, double sums, a double uniform, the
-// proposal recorded for rejection sampling): one wave; per position the row
-// after the slot drawn before, one caller-supplied uniform per row.
+// Parts 3 and 4 of the draft step: the candidate scorer (one workgroup per
+// position and request) and the walk (one workgroup per request, every request
+// in one launch).  The device functions they run, and the pages they follow,
+// are in lattice_dev.hpp.
 
 #include "common.hpp"
 #include "internal.hpp"
-#include "../../include/dflash_draft.h"
-
-#include <math.h>
+#include "lattice_dev.hpp"
 
 namespace dflash {
 
 namespace {
 
-constexpr int kPairThreads = 512;   // eight waves: two per quadrant of S, one per half of the rank
-constexpr int kGateThreads = 256;   // threads of the gate's dot product
-constexpr int kRankSlice = 256;   // rank elements staged per round
-constexpr int kPitch = kRankSlice + 4;   // LDS row pitch (floats): 16 consecutive rows hit distinct banks
-
-__device__ __forceinline__ void row_range(const int32_t* row_offsets, int req, int L, int M, int& a, int& n) {
-    if (row_offsets) {
-        int lo = row_offsets[req], hi = row_offsets[req + 1];
-        lo = min(max(lo, 0), M);
-        hi = min(max(hi, lo), M);
-        a = lo;
-        n = min(hi - lo, L);
-    } else {
-        a = req * L;
-        n = L;
-    }
-}
-
-__device__ __forceinline__ int64_t clamp_tok(int64_t t, int Vt) {
-    return t < 0 ? 0 : (t >= Vt ? (int64_t)Vt - 1 : t);
-}
-
-__global__ void __launch_bounds__(kPairThreads) pair_scores_kernel(
-    const int64_t* __restrict__ cand_tok, const float* __restrict__ tables, const float* __restrict__ gate_w,
-    const uint16_t* __restrict__ hidden, const int64_t* __restrict__ last_tok,
-    const int32_t* __restrict__ row_offsets, int L, int M, int H, int Vt, int K, int r,
-    float* __restrict__ pair) {
-    __shared__ __attribute__((aligned(16))) float As[64][kPitch];
-    __shared__ __attribute__((aligned(16))) float Bs[64][kPitch];
-    __shared__ int64_t prev_row[64], cand_row[64];
-    __shared__ float red[kGateThreads / 64];
-
+__global__ void __launch_bounds__(kPairThreads) pair_scores_kernel(PairArgs A) {
+    __shared__ PairSmem s;
     const int p = blockIdx.x, req = blockIdx.y;
-    const int tid = threadIdx.x;
     int a, n;
-    row_range(row_offsets, req, L, M, a, n);
+    row_range(A.row_offsets, req, A.L, A.M, a, n);
     if (p >= n) return;
-    const int m = a + p;
-
-    const int Jn = (p == 0) ? 1 : K;
-    if (tid < 64) {
-        const int64_t prev = (p == 0) ? last_tok[req] : (tid < K ? cand_tok[(int64_t)(m - 1) * K + tid] : 0);
-        prev_row[tid] = clamp_tok(prev, Vt) * r;
-        const int64_t cand = tid < K ? cand_tok[(int64_t)m * K + tid] : 0;
-        cand_row[tid] = clamp_tok(cand, Vt) * r;
-    }
-
-    float g = 1.f;
-    if (gate_w) {
-        float part = 0.f;
-        const uint16_t* h = hidden + (int64_t)m * H;
-        if (tid < kGateThreads) {
-            for (int i = tid; i < H; i += kGateThreads) part += gate_w[i] * bf16_bits_to_float(h[i]);
-            part = wave_sum(part);
-            if ((tid & 63) == 0) red[tid >> 6] = part;
-        }
-    }
-    __syncthreads();
-    if (gate_w) {
-        const float x = (red[0] + red[1]) + (red[2] + red[3]);
-        g = 1.f / (1.f + expf(-x));
-    }
-
-    const float* TA = tables;
-    const float* TB = tables + (int64_t)Vt * r;
-    // waves w and w + 4 compute the 32 x 32 quadrant (jt, kt) = ((w % 4) / 2, w % 2) of S
-    // on the matrix cores (v_mfma_f32_32x32x2_f32, fp32 products and sums), over the first
-    // and the second half of every rank slice: in MFMA step s lane l supplies
-    // A[prev 32 jt + l % 32][k] and B[cand 32 kt + l % 32][k] with k = 8 (s / 4) + 4 (l / 32)
-    // + s % 4, the same in both, read as float4 from the LDS rows; the two partial sums
-    // are added once at the end (first half + second half)
-    const int lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int lr = lane & 31, lh = lane >> 5;
-    const int quad = wv & 3, half = wv >> 2;
-    const int jt = quad >> 1, kt = quad & 1;
-    f32x16 acc = f32x16{};
-
-    // With r % 4 == 0 and 16-byte aligned tables every row is read as float4:
-    // float4 f of a slice is row f / 64 (A rows, then B rows), elements 4 (f % 64) ..
-    const bool vec = (r & 3) == 0 && (reinterpret_cast<uintptr_t>(tables) & 15) == 0;
-    for (int i0 = 0; i0 < r; i0 += kRankSlice) {
-        const int w = min(kRankSlice, r - i0);        // rank elements of this slice
-        if (vec) {
-            constexpr int kPer = 2 * 64 * kRankSlice / 4 / kPairThreads;   // float4 per thread
-            f32x4 v[kPer];
-#pragma unroll
-            for (int i = 0; i < kPer; ++i) {
-                const int f = tid + i * kPairThreads;       // 0 .. 8191
-                const int b = f >> 12, row = (f >> 6) & 63, c = (f & 63) * 4;
-                const bool ok = row < (b ? K : Jn) && c < w;
-                const float* src = (b ? TB + cand_row[row] : TA + prev_row[row]) + i0 + c;
-                v[i] = ok ? *reinterpret_cast<const f32x4*>(src) : f32x4{0.f, 0.f, 0.f, 0.f};
-            }
-#pragma unroll
-            for (int i = 0; i < kPer; ++i) {
-                const int f = tid + i * kPairThreads;
-                const int b = f >> 12, row = (f >> 6) & 63, c = (f & 63) * 4;
-                *reinterpret_cast<f32x4*>(b ? &Bs[row][c] : &As[row][c]) = v[i];
-            }
-        } else {
-            for (int f = tid; f < 2 * 64 * kRankSlice; f += kPairThreads) {
-                const int b = f / (64 * kRankSlice), row = (f / kRankSlice) & 63, c = f % kRankSlice;
-                const bool ok = row < (b ? K : Jn) && c < w;
-                const float v = ok ? (b ? TB[cand_row[row] + i0 + c] : TA[prev_row[row] + i0 + c]) : 0.f;
-                if (b) Bs[row][c] = v; else As[row][c] = v;
-            }
-        }
-        __syncthreads();
-        const int w8 = (w + 7) >> 3;                  // elements past w are zero in both operands
-        const int gmid = (w8 + 1) >> 1;
-        const float* arow = &As[32 * jt + lr][4 * lh];
-        const float* brow = &Bs[32 * kt + lr][4 * lh];
-        for (int gi = half ? gmid : 0; gi < (half ? w8 : gmid); ++gi) {
-            const f32x4 av = *reinterpret_cast<const f32x4*>(arow + 8 * gi);
-            const f32x4 bv = *reinterpret_cast<const f32x4*>(brow + 8 * gi);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av[e], bv[e], acc, 0, 0, 0);
-        }
-        __syncthreads();
-    }
-
-    // the second-half waves hand their sums to the first-half waves through LDS (As is
-    // free after the last slice's barrier): register i of lane l at float 1024 quad + 64 i + l
-    float* xch = &As[0][0];
-    if (half) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) xch[1024 * quad + 64 * i + lane] = acc[i];
-    }
-    __syncthreads();
-    if (half) return;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] += xch[1024 * quad + 64 * i + lane];
-
-    // register i of lane l: S[32 jt + 8 (i / 4) + 4 (l / 32) + i % 4][32 kt + l % 32]
-    float* out = pair + (int64_t)m * K * K;
-    const int k = 32 * kt + lr;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int j = 32 * jt + 8 * (i / 4) + 4 * lh + i % 4;
-        if (j < K && k < K) out[(int64_t)j * K + k] = (j < Jn) ? g * acc[i] : 0.f;
-    }
+    pair_position(A, req, a, p, s);
 }
 
-constexpr int kWalkThreads = 256;
-constexpr int kWalkSampled = 2;   // the sampled walk (its own entry points; not a dims.walk value)
-constexpr int kWalkChunk = 4;     // positions of S and u per LDS buffer; two buffers
-
-__global__ void __launch_bounds__(kWalkThreads) walk_kernel(const int64_t* __restrict__ cand_tok,
-                                                            const float* __restrict__ unary,
-                                                            const float* __restrict__ pair,
-                                                            const int32_t* __restrict__ row_offsets, int L, int M,
-                                                            int K, int walk, const double* __restrict__ uniforms,
-                                                            float temperature, int64_t* __restrict__ tokens,
-                                                            float* __restrict__ scores,
-                                                            int32_t* __restrict__ slots, double* __restrict__ qprob) {
-    __shared__ __attribute__((aligned(16))) float Ss[2][kWalkChunk][64 * 64];
-    __shared__ float Us[2][kWalkChunk][64];
-    __shared__ float qbest[2][4][64];
-    __shared__ int qarg[2][4][64];
-    __shared__ uint8_t back[DFLASH_MAX_BLOCK_LEN][64];
-    __shared__ __attribute__((aligned(16))) float dsh[4][64];   // delta of the previous position, one row per wave
-    __shared__ int path[DFLASH_MAX_BLOCK_LEN];
-    __shared__ float s_score;
-    const int req = blockIdx.x, tid = threadIdx.x;
-    const int lane = tid & 63, q = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform quarter
-    int a, n;
-    row_range(row_offsets, req, L, M, a, n);
-    if (n <= 0) {
-        if (tid == 0) scores[req] = 0.f;
-        return;
-    }
-    const bool act = lane < K;
-    const int KK = K * K;
-    const bool vec = K == 64 && (reinterpret_cast<uintptr_t>(pair) & 15) == 0;
-
-    // Staging of positions c0 .. c0 + cn into buffer `buf`.  With K = 64 every thread
-    // moves 16 float4 of S (one chunk = 4 x 16 KB): the loads of chunk c + 1 are issued
-    // before chunk c is walked and stored after it.
-    f32x4 sv[kWalkChunk * 4];
-    float uv = 0.f;
-    auto load_chunk = [&](int c0) {
-        const int cn = min(kWalkChunk, n - c0);
-        const f32x4* src = reinterpret_cast<const f32x4*>(pair + (int64_t)(a + c0) * KK);
-#pragma unroll
-        for (int i = 0; i < kWalkChunk * 4; ++i) {
-            const int e = tid + i * kWalkThreads;
-            if (e < cn * 1024) sv[i] = src[e];
-        }
-        uv = tid < cn * K ? unary[(int64_t)(a + c0) * K + tid] : 0.f;
-    };
-    auto store_chunk = [&](int c0, int buf) {
-        const int cn = min(kWalkChunk, n - c0);
-#pragma unroll
-        for (int i = 0; i < kWalkChunk * 4; ++i) {
-            const int e = tid + i * kWalkThreads;
-            if (e < cn * 1024) reinterpret_cast<f32x4*>(&Ss[buf][0][0])[e] = sv[i];
-        }
-        if (tid < cn * K) Us[buf][tid / K][tid % K] = uv;
-    };
-    auto stage_generic = [&](int c0, int buf) {
-        const int cn = min(kWalkChunk, n - c0);
-        const float* src = pair + (int64_t)(a + c0) * KK;
-        for (int e = tid; e < cn * KK; e += kWalkThreads) {
-            const int pp = e / KK, o = e - pp * KK;
-            Ss[buf][pp][(o / K) * 64 + (o % K)] = src[e];
-        }
-        for (int e = tid; e < cn * K; e += kWalkThreads) Us[buf][e / K][e % K] = unary[(int64_t)(a + c0) * K + e];
-    };
-
-    if (vec) { load_chunk(0); store_chunk(0, 0); } else { stage_generic(0, 0); }
-    __syncthreads();
-
-    // Viterbi: every wave keeps delta of the previous position in lane k (d), reads
-    // delta(j) by readlane, takes the best over its quarter j in [16 q, 16 q + 16),
-    // and after one barrier combines the four quarters in order (strict >).
-    float d = -INFINITY;
-    int prev = 0;            // greedy: slot of the previous position (wave 0)
-    float total = 0.f;       // greedy: running score (wave 0)
-    int par = 0;             // parity of the qbest buffers
-    for (int c0 = 0, buf = 0; c0 < n; c0 += kWalkChunk, buf ^= 1) {
-        const int cn = min(kWalkChunk, n - c0);
-        const bool more = c0 + kWalkChunk < n;
-        if (more && vec) load_chunk(c0 + kWalkChunk);
-        for (int pp = 0; pp < cn; ++pp) {
-            const int p = c0 + pp;
-            if (walk == DFLASH_WALK_VITERBI) {
-                if (p == 0) {
-                    d = act ? Us[buf][0][lane] + Ss[buf][0][lane] : -INFINITY;
-                } else {
-                    // the 16 S entries of this quarter and the 16 delta(j) first (independent
-                    // LDS reads and readlanes), then a tree over (value, j) in which the
-                    // higher j wins only by strict >: the lowest j reaching the maximum, as an
-                    // ascending scan with strict > (slots past K are -inf)
-                    float sv[16], vv[16];
-                    int jj[16];
-                    // delta(j) of the quarter reaches every lane through the wave's own LDS row
-                    // (one write, four broadcast reads): in-order LDS access within a wave
-                    // needs no barrier
-                    dsh[q][lane] = d;
-#pragma unroll
-                    for (int t = 0; t < 16; ++t) sv[t] = Ss[buf][pp][(16 * q + t) * 64 + lane];
-                    const f32x4* drow = reinterpret_cast<const f32x4*>(&dsh[q][16 * q]);
-                    const f32x4 d0 = drow[0], d1 = drow[1], d2 = drow[2], d3 = drow[3];
-                    // every LDS read above is issued before the first sum below uses one
-                    __builtin_amdgcn_sched_barrier(0);
-                    const float dq[16] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3],
-                                          d2[0], d2[1], d2[2], d2[3], d3[0], d3[1], d3[2], d3[3]};
-#pragma unroll
-                    for (int t = 0; t < 16; ++t) {
-                        const int j = 16 * q + t;
-                        vv[t] = j < K ? dq[t] + sv[t] : -INFINITY;
-                        jj[t] = j;
-                    }
-#pragma unroll
-                    for (int w = 1; w < 16; w *= 2)
-#pragma unroll
-                        for (int t = 0; t < 16; t += 2 * w)
-                            if (vv[t + w] > vv[t]) { vv[t] = vv[t + w]; jj[t] = jj[t + w]; }
-                    const float best = vv[0];
-                    const int arg = jj[0];
-                    qbest[par][q][lane] = best;
-                    qarg[par][q][lane] = arg;
-                    __syncthreads();
-                    float bb = qbest[par][0][lane];
-                    int ar = qarg[par][0][lane];
-#pragma unroll
-                    for (int qq = 1; qq < 4; ++qq)
-                        if (qbest[par][qq][lane] > bb) { bb = qbest[par][qq][lane]; ar = qarg[par][qq][lane]; }
-                    if (bb == -INFINITY) ar = 0;   // nothing finite to extend: slot 0, as a scan from j = 0
-                    d = act ? Us[buf][pp][lane] + bb : -INFINITY;
-                    if (q == 0) back[p][lane] = (uint8_t)min(ar, K - 1);
-                    par ^= 1;
-                }
-            } else if (walk == kWalkSampled) {
-                if (tid < 64) {
-                    // the row after the slot drawn before, in fp32; float weights (the fp32
-                    // rounding of exp, taken in double); running and total sums in double in
-                    // slot order; the smallest slot whose running sum exceeds U * total
-                    const float v = act ? Us[buf][pp][lane] + Ss[buf][pp][prev * 64 + lane] : -INFINITY;
-                    const float xs = act ? v / temperature : -INFINITY;
-                    const float mx = wave_max(xs);
-                    const float wf = act ? (float)exp((double)(xs - mx)) : 0.f;
-                    // one sequential pass in slot order: lane k keeps the running sum W_k, and
-                    // W_{K-1} is the total; the draw is the lowest lane with U * total < W_k
-                    double run = 0.0, mine = 0.0;
-                    for (int k = 0; k < K; ++k) {
-                        run += (double)__int_as_float(__builtin_amdgcn_readlane(__float_as_int(wf), k));
-                        mine = lane == k ? run : mine;
-                    }
-                    const double tot = run;
-                    const double thr = uniforms[a + p] * tot;
-                    const int c = min(lowest_lane(act && thr < mine), K - 1);
-                    if (qprob && act) qprob[(int64_t)(a + p) * K + lane] = (double)wf / tot;
-                    total += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), c));
-                    if (lane == 0) path[p] = c;
-                    prev = c;
-                }
-            } else if (tid < 64) {
-                const float v = act ? Us[buf][pp][lane] + Ss[buf][pp][prev * 64 + lane] : -INFINITY;
-                const float mx = wave_max(v);
-                const int c = min(lowest_lane(act && v == mx), K - 1);
-                total += mx;
-                if (lane == 0) path[p] = c;
-                prev = c;
-            }
-        }
-        if (more) {
-            __syncthreads();    // everyone is done with buffer buf ^ 1 (walked two chunks ago)
-            if (vec) store_chunk(c0 + kWalkChunk, buf ^ 1); else stage_generic(c0 + kWalkChunk, buf ^ 1);
-            __syncthreads();
-        }
-    }
-    if (tid < 64) {
-        float score;
-        if (walk == DFLASH_WALK_VITERBI) {
-            score = wave_max(d);
-            // NaN scores match no lane: fall back to slot 0 rather than index past the slots
-            const int last = min(lowest_lane(act && d == score), K - 1);
-            if (lane == 0) {
-                int c = last;
-                for (int p = n - 1; p >= 0; --p) {
-                    path[p] = c;
-                    if (p > 0) c = min((int)back[p][c], K - 1);
-                }
-            }
-        } else {
-            score = total;
-        }
-        if (lane == 0) s_score = score;
-    }
-    __syncthreads();
-    if (tid == 0) scores[req] = s_score;
-    for (int p = tid; p < n; p += kWalkThreads) {
-        const int c = path[p];
-        tokens[a + p] = cand_tok[(int64_t)(a + p) * K + c];
-        if (slots) slots[a + p] = c;
-    }
+__global__ void __launch_bounds__(kLatThreads) walk_kernel(WalkArgs A) {
+    __shared__ WalkSmem s;
+    walk_request(A, blockIdx.x, s);
 }
 
 }  // namespace
@@ -381,8 +31,8 @@ hipError_t launch_pair_scores(const int64_t* cand_tok, const float* tables, cons
                               const uint16_t* hidden, const int64_t* last_tok, const int32_t* row_offsets,
                               int R, int L, int M, int H, int Vt, int K, int r, float* pair, hipStream_t s) {
     if (R <= 0 || M <= 0) return hipSuccess;
-    hipLaunchKernelGGL(pair_scores_kernel, dim3(L, R), dim3(kPairThreads), 0, s, cand_tok, tables, gate_w, hidden,
-                       last_tok, row_offsets, L, M, H, Vt, K, r, pair);
+    const PairArgs A{cand_tok, tables, gate_w, hidden, last_tok, row_offsets, L, M, H, Vt, K, r, pair};
+    hipLaunchKernelGGL(pair_scores_kernel, dim3(L, R), dim3(kPairThreads), 0, s, A);
     return hipGetLastError();
 }
 
@@ -390,8 +40,8 @@ hipError_t launch_walk(const int64_t* cand_tok, const float* unary, const float*
                        int R, int L, int M, int K, int walk, int64_t* tokens, float* scores, int32_t* slots,
                        hipStream_t s) {
     if (R <= 0) return hipSuccess;
-    hipLaunchKernelGGL(walk_kernel, dim3(R), dim3(kWalkThreads), 0, s, cand_tok, unary, pair, row_offsets, L, M, K,
-                       walk, nullptr, 1.f, tokens, scores, slots, nullptr);
+    const WalkArgs A{cand_tok, unary, pair, row_offsets, L, M, K, walk, nullptr, 1.f, tokens, scores, slots, nullptr};
+    hipLaunchKernelGGL(walk_kernel, dim3(R), dim3(kLatThreads), 0, s, A);
     return hipGetLastError();
 }
 
@@ -400,8 +50,9 @@ hipError_t launch_walk_sampled(const int64_t* cand_tok, const float* unary, cons
                                float temperature, int64_t* tokens, float* scores, int32_t* slots, double* q,
                                hipStream_t s) {
     if (R <= 0) return hipSuccess;
-    hipLaunchKernelGGL(walk_kernel, dim3(R), dim3(kWalkThreads), 0, s, cand_tok, unary, pair, row_offsets, L, M, K,
-                       kWalkSampled, uniforms, temperature, tokens, scores, slots, q);
+    const WalkArgs A{cand_tok, unary, pair, row_offsets, L, M, K, kWalkSampled, uniforms, temperature, tokens,
+                     scores, slots, q};
+    hipLaunchKernelGGL(walk_kernel, dim3(R), dim3(kLatThreads), 0, s, A);
     return hipGetLastError();
 }
 

@@ -1,0 +1,398 @@
+// Parts 3 and 4 of the draft step as device functions of one workgroup, run by
+// the kernels of lattice.hip: the Markov-head candidate scorer over the packed
+// Top-K lattice and the walk through it.
+//
+// Scorer (optimum-intel page "Export DFlash v2 and DSpark drafts ...", What
+// does this PR do?: the Top-K lattice of the DSpark head, with transitions
+// gated by the draft hidden states for DFlash v2; openvino.genai page "Add
+// DSpark and DFlash v2 drafts ...", commit "DFlash-2 Markov head /
+// BlockRowSource": one run over the packed block rows of all requests):
+//   S_p[j][k] = g_p * <A[t_{p-1}[j]], B[t_p[k]]>,  S_0[0][k] = g_0 * <A[last], B[t_0[k]]>,
+//   g_p = sigmoid(w . h_p) when gated, else 1.
+// One workgroup per (position, request).  The K rows of A and of B it needs
+// are gathered whole (up to 256 rank elements at a time), every load in flight
+// at once, into LDS rows of 260 floats (the 32 rows a wave reads fall in
+// distinct banks); eight waves compute S with fp32 MFMAs, two per 32 x 32
+// quadrant, each over one half of the rank.
+//
+// Walk (same commit: the greedy walk takes the best candidate after the token
+// before; the max-score walk is its Viterbi form): one 256-thread workgroup per
+// request stages up to eight positions of S and u in LDS at a time.  Viterbi:
+// thread (k, q) takes the best delta(j) + S[j][k] over j in its quarter q of
+// the slots (ascending, strict >), and the quarters are combined in order, so
+// the lowest j wins a tie; back-pointers stay in LDS.  Greedy: one wave, an
+// argmax per position (DPP max reduction, lowest lane of a ballot).  Sampled
+// (same commit: a sampled request walks the lattice with its draft RNG; the
+// sampled-drafting commits: float weights, double sums, a double uniform, the
+// proposal recorded for rejection sampling): one wave; per position the row
+// after the slot drawn before, one caller-supplied uniform per row.
+#pragma once
+
+#include "common.hpp"
+#include "../../include/dflash_draft.h"
+
+#include <math.h>
+
+namespace dflash {
+
+namespace {
+
+constexpr int kLatThreads = 256;    // threads of a walk workgroup: four waves
+constexpr int kPairThreads = 512;   // threads of a scorer workgroup: eight waves
+constexpr int kGateThreads = 256;   // threads of the gate's dot product
+constexpr int kRankSlice = 256;     // rank elements staged per round
+constexpr int kPitch = kRankSlice + 4;   // LDS row pitch (floats): 16 consecutive rows hit distinct banks
+constexpr int kWalkSampled = 2;     // the sampled walk (its own entry points; not a dims.walk value)
+constexpr int kWalkChunk = 4;       // positions of S and u per LDS buffer; two buffers
+
+// Rows of request req: [a, a + n), n at most L (uniform blocks of L rows without offsets).
+__device__ __forceinline__ void row_range(const int32_t* row_offsets, int req, int L, int M, int& a, int& n) {
+    if (row_offsets) {
+        int lo = row_offsets[req], hi = row_offsets[req + 1];
+        lo = min(max(lo, 0), M);
+        hi = min(max(hi, lo), M);
+        a = lo;
+        n = min(hi - lo, L);
+    } else {
+        a = req * L;
+        n = L;
+    }
+}
+
+__device__ __forceinline__ int64_t clamp_tok(int64_t t, int Vt) {
+    return t < 0 ? 0 : (t >= Vt ? (int64_t)Vt - 1 : t);
+}
+
+struct PairArgs {
+    const int64_t* cand_tok;     // [M][K] target ids of the slots
+    const float* tables;         // [2][Vt][r]
+    const float* gate_w;         // [H] or null
+    const uint16_t* hidden;      // [M][H] bf16 (read when gated)
+    const int64_t* last_tok;     // [R]
+    const int32_t* row_offsets;  // [R+1] or null
+    int L, M, H, Vt, K, r;
+    float* pair;                 // out [M][K][K]
+};
+
+struct PairSmem {
+    __attribute__((aligned(16))) float As[64][kPitch];
+    __attribute__((aligned(16))) float Bs[64][kPitch];
+    int64_t prev_row[64], cand_row[64];
+    float red[4];
+};
+
+// S of position p of request req, whose rows start at row a (row m = a + p), into pair[m];
+// by a workgroup of kPairThreads threads (eight waves: two per 32 x 32 quadrant of S, one
+// per half of the rank).
+__device__ __forceinline__ void pair_position(const PairArgs& A, int req, int a, int p, PairSmem& s) {
+    const int tid = threadIdx.x;
+    const int m = a + p;
+    const int K = A.K, r = A.r, Vt = A.Vt, H = A.H;
+    const int Jn = (p == 0) ? 1 : K;
+    if (tid < 64) {
+        const int64_t prev = (p == 0) ? A.last_tok[req] : (tid < K ? A.cand_tok[(int64_t)(m - 1) * K + tid] : 0);
+        s.prev_row[tid] = clamp_tok(prev, Vt) * r;
+        const int64_t cand = tid < K ? A.cand_tok[(int64_t)m * K + tid] : 0;
+        s.cand_row[tid] = clamp_tok(cand, Vt) * r;
+    }
+    if (A.gate_w && tid < kGateThreads) {
+        float part = 0.f;
+        const uint16_t* h = A.hidden + (int64_t)m * H;
+        for (int i = tid; i < H; i += kGateThreads) part += A.gate_w[i] * bf16_bits_to_float(h[i]);
+        part = wave_sum(part);
+        if ((tid & 63) == 0) s.red[tid >> 6] = part;
+    }
+    __syncthreads();
+    float g = 1.f;
+    if (A.gate_w) {
+        const float x = (s.red[0] + s.red[1]) + (s.red[2] + s.red[3]);
+        g = 1.f / (1.f + expf(-x));
+    }
+
+    const float* TA = A.tables;
+    const float* TB = A.tables + (int64_t)Vt * r;
+    // waves w and w + 4 compute the 32 x 32 quadrant (jt, kt) = ((w % 4) / 2, w % 2) of S
+    // on the matrix cores (v_mfma_f32_32x32x2_f32, fp32 products and sums), over the first
+    // and the second half of every rank slice: in MFMA step s lane l supplies
+    // A[prev 32 jt + l % 32][k] and B[cand 32 kt + l % 32][k] with k = 8 (s / 4) + 4 (l / 32)
+    // + s % 4, the same in both, read as float4 from the LDS rows; the two partial sums
+    // are added once at the end (first half + second half)
+    const int lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lr = lane & 31, lh = lane >> 5;
+    const int quad = wv & 3, half = wv >> 2;
+    const int jt = quad >> 1, kt = quad & 1;
+    f32x16 acc = f32x16{};
+
+    // With r % 4 == 0 and 16-byte aligned tables every row is read as float4:
+    // float4 f of a slice is row f / 64 (A rows, then B rows), elements 4 (f % 64) ..
+    const bool vec = (r & 3) == 0 && (reinterpret_cast<uintptr_t>(A.tables) & 15) == 0;
+    for (int i0 = 0; i0 < r; i0 += kRankSlice) {
+        const int w = min(kRankSlice, r - i0);        // rank elements of this slice
+        if (vec) {
+            constexpr int kPer = 2 * 64 * kRankSlice / 4 / kPairThreads;   // float4 per thread
+            f32x4 v[kPer];
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) {
+                const int f = tid + i * kPairThreads;       // 0 .. 8191
+                const int b = f >> 12, row = (f >> 6) & 63, c = (f & 63) * 4;
+                const bool ok = row < (b ? K : Jn) && c < w;
+                const float* src = (b ? TB + s.cand_row[row] : TA + s.prev_row[row]) + i0 + c;
+                v[i] = ok ? *reinterpret_cast<const f32x4*>(src) : f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) {
+                const int f = tid + i * kPairThreads;
+                const int b = f >> 12, row = (f >> 6) & 63, c = (f & 63) * 4;
+                *reinterpret_cast<f32x4*>(b ? &s.Bs[row][c] : &s.As[row][c]) = v[i];
+            }
+        } else {
+            for (int f = tid; f < 2 * 64 * kRankSlice; f += kPairThreads) {
+                const int b = f / (64 * kRankSlice), row = (f / kRankSlice) & 63, c = f % kRankSlice;
+                const bool ok = row < (b ? K : Jn) && c < w;
+                const float v = ok ? (b ? TB[s.cand_row[row] + i0 + c] : TA[s.prev_row[row] + i0 + c]) : 0.f;
+                if (b) s.Bs[row][c] = v; else s.As[row][c] = v;
+            }
+        }
+        __syncthreads();
+        const int w8 = (w + 7) >> 3;                  // elements past w are zero in both operands
+        const int gmid = (w8 + 1) >> 1;
+        const float* arow = &s.As[32 * jt + lr][4 * lh];
+        const float* brow = &s.Bs[32 * kt + lr][4 * lh];
+        for (int gi = half ? gmid : 0; gi < (half ? w8 : gmid); ++gi) {
+            const f32x4 av = *reinterpret_cast<const f32x4*>(arow + 8 * gi);
+            const f32x4 bv = *reinterpret_cast<const f32x4*>(brow + 8 * gi);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av[e], bv[e], acc, 0, 0, 0);
+        }
+        __syncthreads();
+    }
+
+    // the second-half waves hand their sums to the first-half waves through LDS (As is
+    // free after the last slice's barrier): register i of lane l at float 1024 quad + 64 i + l
+    float* xch = &s.As[0][0];
+    if (half) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) xch[1024 * quad + 64 * i + lane] = acc[i];
+    }
+    __syncthreads();
+    if (half) return;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] += xch[1024 * quad + 64 * i + lane];
+
+    // register i of lane l: S[32 jt + 8 (i / 4) + 4 (l / 32) + i % 4][32 kt + l % 32]
+    float* out = A.pair + (int64_t)m * K * K;
+    const int k = 32 * kt + lr;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int j = 32 * jt + 8 * (i / 4) + 4 * lh + i % 4;
+        if (j < K && k < K) out[(int64_t)j * K + k] = (j < Jn) ? g * acc[i] : 0.f;
+    }
+}
+
+struct WalkArgs {
+    const int64_t* cand_tok;     // [M][K]
+    const float* unary;          // [M][K]
+    const float* pair;           // [M][K][K]
+    const int32_t* row_offsets;  // [R+1] or null
+    int L, M, K, walk;           // walk: DFLASH_WALK_VITERBI, DFLASH_WALK_GREEDY or kWalkSampled
+    const double* uniforms;      // [M] (sampled)
+    float temperature;           // (sampled)
+    int64_t* tokens;             // out [M]
+    float* scores;               // out [R]
+    int32_t* slots;              // out [M] or null
+    double* qprob;               // out [M][K] or null (sampled)
+};
+
+struct WalkSmem {
+    __attribute__((aligned(16))) float Ss[2][kWalkChunk][64 * 64];
+    float Us[2][kWalkChunk][64];
+    float qbest[2][4][64];
+    int qarg[2][4][64];
+    uint8_t back[DFLASH_MAX_BLOCK_LEN][64];
+    __attribute__((aligned(16))) float dsh[4][64];   // delta of the previous position, one row per wave
+    int path[DFLASH_MAX_BLOCK_LEN];
+    float s_score;
+};
+
+// The walk of request req through its lattice; writes tokens, scores (and slots, q).
+__device__ __forceinline__ void walk_request(const WalkArgs& A, int req, WalkSmem& s) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, q = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform quarter
+    const int K = A.K, walk = A.walk;
+    int a, n;
+    row_range(A.row_offsets, req, A.L, A.M, a, n);
+    if (n <= 0) {
+        if (tid == 0) A.scores[req] = 0.f;
+        return;
+    }
+    const bool act = lane < K;
+    const int KK = K * K;
+    const bool vec = K == 64 && (reinterpret_cast<uintptr_t>(A.pair) & 15) == 0;
+
+    // Staging of positions c0 .. c0 + cn into buffer `buf`.  With K = 64 every thread
+    // moves 16 float4 of S (one chunk = 4 x 16 KB): the loads of chunk c + 1 are issued
+    // before chunk c is walked and stored after it.
+    f32x4 sv[kWalkChunk * 4];
+    float uv = 0.f;
+    auto load_chunk = [&](int c0) {
+        const int cn = min(kWalkChunk, n - c0);
+        const f32x4* src = reinterpret_cast<const f32x4*>(A.pair + (int64_t)(a + c0) * KK);
+#pragma unroll
+        for (int i = 0; i < kWalkChunk * 4; ++i) {
+            const int e = tid + i * kLatThreads;
+            if (e < cn * 1024) sv[i] = src[e];
+        }
+        uv = tid < cn * K ? A.unary[(int64_t)(a + c0) * K + tid] : 0.f;
+    };
+    auto store_chunk = [&](int c0, int buf) {
+        const int cn = min(kWalkChunk, n - c0);
+#pragma unroll
+        for (int i = 0; i < kWalkChunk * 4; ++i) {
+            const int e = tid + i * kLatThreads;
+            if (e < cn * 1024) reinterpret_cast<f32x4*>(&s.Ss[buf][0][0])[e] = sv[i];
+        }
+        if (tid < cn * K) s.Us[buf][tid / K][tid % K] = uv;
+    };
+    auto stage_generic = [&](int c0, int buf) {
+        const int cn = min(kWalkChunk, n - c0);
+        const float* src = A.pair + (int64_t)(a + c0) * KK;
+        for (int e = tid; e < cn * KK; e += kLatThreads) {
+            const int pp = e / KK, o = e - pp * KK;
+            s.Ss[buf][pp][(o / K) * 64 + (o % K)] = src[e];
+        }
+        for (int e = tid; e < cn * K; e += kLatThreads) s.Us[buf][e / K][e % K] = A.unary[(int64_t)(a + c0) * K + e];
+    };
+
+    if (vec) { load_chunk(0); store_chunk(0, 0); } else { stage_generic(0, 0); }
+    __syncthreads();
+
+    // Viterbi: every wave keeps delta of the previous position in lane k (d), reads
+    // delta(j) by readlane, takes the best over its quarter j in [16 q, 16 q + 16),
+    // and after one barrier combines the four quarters in order (strict >).
+    float d = -INFINITY;
+    int prev = 0;            // greedy: slot of the previous position (wave 0)
+    float total = 0.f;       // greedy: running score (wave 0)
+    int par = 0;             // parity of the qbest buffers
+    for (int c0 = 0, buf = 0; c0 < n; c0 += kWalkChunk, buf ^= 1) {
+        const int cn = min(kWalkChunk, n - c0);
+        const bool more = c0 + kWalkChunk < n;
+        if (more && vec) load_chunk(c0 + kWalkChunk);
+        for (int pp = 0; pp < cn; ++pp) {
+            const int p = c0 + pp;
+            if (walk == DFLASH_WALK_VITERBI) {
+                if (p == 0) {
+                    d = act ? s.Us[buf][0][lane] + s.Ss[buf][0][lane] : -INFINITY;
+                } else {
+                    // the 16 S entries of this quarter and the 16 delta(j) first (independent
+                    // LDS reads and readlanes), then a tree over (value, j) in which the
+                    // higher j wins only by strict >: the lowest j reaching the maximum, as an
+                    // ascending scan with strict > (slots past K are -inf)
+                    float svq[16], vv[16];
+                    int jj[16];
+                    // delta(j) of the quarter reaches every lane through the wave's own LDS row
+                    // (one write, four broadcast reads): in-order LDS access within a wave
+                    // needs no barrier
+                    s.dsh[q][lane] = d;
+#pragma unroll
+                    for (int t = 0; t < 16; ++t) svq[t] = s.Ss[buf][pp][(16 * q + t) * 64 + lane];
+                    const f32x4* drow = reinterpret_cast<const f32x4*>(&s.dsh[q][16 * q]);
+                    const f32x4 d0 = drow[0], d1 = drow[1], d2 = drow[2], d3 = drow[3];
+                    // every LDS read above is issued before the first sum below uses one
+                    __builtin_amdgcn_sched_barrier(0);
+                    const float dq[16] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3],
+                                          d2[0], d2[1], d2[2], d2[3], d3[0], d3[1], d3[2], d3[3]};
+#pragma unroll
+                    for (int t = 0; t < 16; ++t) {
+                        const int j = 16 * q + t;
+                        vv[t] = j < K ? dq[t] + svq[t] : -INFINITY;
+                        jj[t] = j;
+                    }
+#pragma unroll
+                    for (int w = 1; w < 16; w *= 2)
+#pragma unroll
+                        for (int t = 0; t < 16; t += 2 * w)
+                            if (vv[t + w] > vv[t]) { vv[t] = vv[t + w]; jj[t] = jj[t + w]; }
+                    const float best = vv[0];
+                    const int arg = jj[0];
+                    s.qbest[par][q][lane] = best;
+                    s.qarg[par][q][lane] = arg;
+                    __syncthreads();
+                    float bb = s.qbest[par][0][lane];
+                    int ar = s.qarg[par][0][lane];
+#pragma unroll
+                    for (int qq = 1; qq < 4; ++qq)
+                        if (s.qbest[par][qq][lane] > bb) { bb = s.qbest[par][qq][lane]; ar = s.qarg[par][qq][lane]; }
+                    if (bb == -INFINITY) ar = 0;   // nothing finite to extend: slot 0, as a scan from j = 0
+                    d = act ? s.Us[buf][pp][lane] + bb : -INFINITY;
+                    if (q == 0) s.back[p][lane] = (uint8_t)min(ar, K - 1);
+                    par ^= 1;
+                }
+            } else if (walk == kWalkSampled) {
+                if (tid < 64) {
+                    // the row after the slot drawn before, in fp32; float weights (the fp32
+                    // rounding of exp, taken in double); running and total sums in double in
+                    // slot order; the smallest slot whose running sum exceeds U * total
+                    const float v = act ? s.Us[buf][pp][lane] + s.Ss[buf][pp][prev * 64 + lane] : -INFINITY;
+                    const float xs = act ? v / A.temperature : -INFINITY;
+                    const float mx = wave_max(xs);
+                    const float wf = act ? (float)exp((double)(xs - mx)) : 0.f;
+                    // one sequential pass in slot order: lane k keeps the running sum W_k, and
+                    // W_{K-1} is the total; the draw is the lowest lane with U * total < W_k
+                    double run = 0.0, mine = 0.0;
+                    for (int k = 0; k < K; ++k) {
+                        run += (double)__int_as_float(__builtin_amdgcn_readlane(__float_as_int(wf), k));
+                        mine = lane == k ? run : mine;
+                    }
+                    const double tot = run;
+                    const double thr = A.uniforms[a + p] * tot;
+                    const int c = min(lowest_lane(act && thr < mine), K - 1);
+                    if (A.qprob && act) A.qprob[(int64_t)(a + p) * K + lane] = (double)wf / tot;
+                    total += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), c));
+                    if (lane == 0) s.path[p] = c;
+                    prev = c;
+                }
+            } else if (tid < 64) {
+                const float v = act ? s.Us[buf][pp][lane] + s.Ss[buf][pp][prev * 64 + lane] : -INFINITY;
+                const float mx = wave_max(v);
+                const int c = min(lowest_lane(act && v == mx), K - 1);
+                total += mx;
+                if (lane == 0) s.path[p] = c;
+                prev = c;
+            }
+        }
+        if (more) {
+            __syncthreads();    // everyone is done with buffer buf ^ 1 (walked two chunks ago)
+            if (vec) store_chunk(c0 + kWalkChunk, buf ^ 1); else stage_generic(c0 + kWalkChunk, buf ^ 1);
+            __syncthreads();
+        }
+    }
+    if (tid < 64) {
+        float score;
+        if (walk == DFLASH_WALK_VITERBI) {
+            score = wave_max(d);
+            // NaN scores match no lane: fall back to slot 0 rather than index past the slots
+            const int last = min(lowest_lane(act && d == score), K - 1);
+            if (lane == 0) {
+                int c = last;
+                for (int p = n - 1; p >= 0; --p) {
+                    s.path[p] = c;
+                    if (p > 0) c = min((int)s.back[p][c], K - 1);
+                }
+            }
+        } else {
+            score = total;
+        }
+        if (lane == 0) s.s_score = score;
+    }
+    __syncthreads();
+    if (tid == 0) A.scores[req] = s.s_score;
+    for (int p = tid; p < n; p += kLatThreads) {
+        const int c = s.path[p];
+        A.tokens[a + p] = A.cand_tok[(int64_t)(a + p) * K + c];
+        if (A.slots) A.slots[a + p] = c;
+    }
+}
+
+}  // namespace
+
+}  // namespace dflash

@@ -1,30 +1,10 @@
-// Part 2 of the draft step: the K = min(64, V_d) best draft tokens of every
-// row in slot order (logit descending, draft id ascending), the d2t remap of
-// draft token i to target token i + d2t[i], and the unary score z - lse
-// (optimum-intel page "Support MiniCPM-OCR-1.0-DSpark", What does this PR
-// do?; the Markov head needs "the radix TopK" on the GPU per the page "Export
-// DFlash v2 and DSpark drafts ...", What does this PR do?; ties ordered by
-// index as in the TopP commit of the openvino.genai page).
-//
-// The top K of a row is read from the maxima of its 32-logit tiles: if tau is
-// at most the K-th largest tile maximum, every member of the top K is >= tau and
-// sits in a tile whose maximum reaches tau, so only those tiles are read
-// (topk_tiles).  The lm_head kernel stores the tile maxima as it writes the
-// logits; for logits from elsewhere one streaming pass (tile_max) computes them.
-// Within a chunk of a row (the exact path for rows with heavy ties), tau is the
-// K-th largest of the 256 per-thread maxima: at least K keys of the chunk are
-// >= tau, and only those survivors (about K + 10 for smooth rows) are ranked,
-// each by counting the survivors that beat it, which yields the slot order
-// directly.  When more than 256 keys survive, an exact radix select on 8-bit
-// digits finds the K-th key instead, and equal keys are taken in id order.
-// Sorted per-chunk lists are merged pairwise in LDS (each entry's merged
-// position = its own index + the number of entries of the other list that beat
-// it, by binary search).
-// Entries are (key << 32 | ~id), so a larger entry is the better slot and
-// every comparison is one 64-bit compare.
+// Part 2 of the draft step as stand-alone kernels: the Top-K of every row
+// (the row's device function is in topk_row.hpp), the streaming pass that
+// computes tile maxima of logits from elsewhere, and the head-less argmax.
 
 #include "common.hpp"
 #include "internal.hpp"
+#include "topk_row.hpp"
 
 #include <math.h>
 
@@ -32,452 +12,9 @@ namespace dflash {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kFastCap = 256;   // survivors ranked directly
-constexpr int kMaxTopK = 64;
-
-__device__ __forceinline__ int block_excl_scan(int v, int* wsum, int& total) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    int x = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(x, o);
-        if (lane >= o) x += y;
-    }
-    if (lane == 63) wsum[w] = x;
-    __syncthreads();
-    int off = 0, tot = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int s = wsum[i];
-        off += (i < w) ? s : 0;
-        tot += s;
-    }
-    __syncthreads();
-    total = tot;
-    return off + x - v;
-}
-
-// Slot-order the n unique entries of list[0..n) and write the first K to out
-// (empty entries fill the rest when n < K).  list[n] must be readable and hold
-// kEmptyEntry when n is odd (it is read in pairs and beats nothing).
-__device__ __forceinline__ void rank_place(const uint64_t* list, int n, int K, uint64_t* out) {
-    const ulonglong2* pairs = reinterpret_cast<const ulonglong2*>(list);
-    const int np = (n + 1) >> 1;
-    if (n <= kThreads / 2) {
-        // two threads per entry, each counting the better entries in one half of the pairs
-        const int i = threadIdx.x >> 1, h = threadIdx.x & 1;
-        const uint64_t my = i < n ? list[i] : 0;
-        const int half = (np + 1) >> 1;
-        const int j0 = h * half, j1 = min(np, j0 + half);
-        int rank = 0;
-#pragma unroll 4
-        for (int j = j0; j < j1; ++j) {
-            const ulonglong2 e = pairs[j];
-            rank += (e.x > my) ? 1 : 0;
-            rank += (e.y > my) ? 1 : 0;
-        }
-        rank += __shfl_xor(rank, 1);
-        if (i < n && h == 0 && rank < K) out[rank] = my;
-        for (int k = n + threadIdx.x; k < K; k += kThreads) out[k] = kEmptyEntry;
-        return;
-    }
-    for (int i = threadIdx.x; i < n; i += kThreads) {
-        const uint64_t my = list[i];
-        int rank = 0;
-#pragma unroll 4
-        for (int j = 0; j < np; ++j) {
-            const ulonglong2 e = pairs[j];
-            rank += (e.x > my) ? 1 : 0;
-            rank += (e.y > my) ? 1 : 0;
-        }
-        if (rank < K) out[rank] = my;
-    }
-    for (int i = n + threadIdx.x; i < K; i += kThreads) out[i] = kEmptyEntry;
-}
-
-// The 64 lanes' values sorted in descending order across the wave (bitonic
-// network over lane pairs); lane i returns the (i+1)-th largest.
-__device__ __forceinline__ uint32_t wave_sort_desc(uint32_t x) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int k = 2; k <= 64; k <<= 1) {
-#pragma unroll
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            const uint32_t y = (uint32_t)__shfl_xor((int)x, j);
-            const bool desc = (lane & k) == 0;
-            const bool lower = (lane & j) == 0;
-            x = (desc == lower) ? max(x, y) : min(x, y);
-        }
-    }
-    return x;
-}
-
-struct ChunkShared {
-    uint32_t wtau[4];
-    __attribute__((aligned(16))) uint64_t cand[kFastCap + 2];
-    uint32_t hist[256];
-    int wsum[4];
-    int s_digit, s_want;
-};
-
-// The K best entries of logits [cbase, cbase + 256 PT) of `row` (ids < V), slot
-// ordered, into out[0..K) (global or LDS).  Called by all 256 threads; uses sh.
-template <int PT>
-__device__ __forceinline__ void chunk_select(const float* __restrict__ row, int cbase, int V, int K,
-                                             uint64_t* out, ChunkShared& sh) {
-    const int tid = threadIdx.x;
-
-    // ---- load PT logits per thread: element (j, q) has id cbase + j*1024 + 4*tid + q
-    uint32_t key[PT];
-#pragma unroll
-    for (int j = 0; j < PT / 4; ++j) {
-        const int v = cbase + j * (4 * kThreads) + 4 * tid;
-        f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        if (v < V) z = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + v));
-#pragma unroll
-        for (int q = 0; q < 4; ++q) key[4 * j + q] = (v + q < V) ? float_to_key(z[q]) : 0u;
-    }
-    auto id_of = [&](int e) { return (uint32_t)(cbase + (e >> 2) * (4 * kThreads) + 4 * tid + (e & 3)); };
-
-    // ---- tau: with q = ceil(K / 4), every wave has q lanes whose maximum is at
-    // least the q-th largest lane maximum of that wave, so at least 4q >= K keys
-    // of the chunk are >= the smallest of the four waves' q-th largest maxima.
-    uint32_t mx = 0;
-#pragma unroll
-    for (int e = 0; e < PT; ++e) mx = max(mx, key[e]);
-    const uint32_t sorted = wave_sort_desc(mx);
-    const int q = (K + 3) >> 2;
-    const uint32_t wq = (uint32_t)__builtin_amdgcn_readlane((int)sorted, q - 1);
-    if ((tid & 63) == 0) sh.wtau[tid >> 6] = wq;
-    __syncthreads();
-    const uint32_t tau = max(min(min(sh.wtau[0], sh.wtau[1]), min(sh.wtau[2], sh.wtau[3])), 1u);   // key 0: past the row
-
-    int cnt = 0;
-#pragma unroll
-    for (int e = 0; e < PT; ++e) cnt += (key[e] >= tau) ? 1 : 0;
-    int n;
-    const int pos = block_excl_scan(cnt, sh.wsum, n);
-
-    if (n <= kFastCap) {
-        int p = pos;
-#pragma unroll
-        for (int e = 0; e < PT; ++e)
-            if (key[e] >= tau && p < kFastCap) sh.cand[p++] = pack_entry(key[e], id_of(e));
-        if (tid == 0) sh.cand[n] = kEmptyEntry;
-        __syncthreads();
-        rank_place(sh.cand, n, K, out);
-        __syncthreads();
-        return;
-    }
-
-    // ---- fallback: exact K-th key by radix select on 8-bit digits
-    if (tid == 0) { sh.s_digit = 0; sh.s_want = 1; }
-    uint32_t prefix = 0, pmask = 0;
-    int want = K;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-        sh.hist[tid] = 0;
-        __syncthreads();
-#pragma unroll
-        for (int e = 0; e < PT; ++e)
-            if (key[e] != 0u && (key[e] & pmask) == prefix) atomicAdd(&sh.hist[(key[e] >> shift) & 255u], 1u);
-        __syncthreads();
-        if (tid == 0) {
-            int cum = 0;
-            for (int d = 255; d >= 0; --d) {
-                const int h = (int)sh.hist[d];
-                if (cum + h >= want) { sh.s_digit = d; sh.s_want = want - cum; break; }
-                cum += h;
-            }
-        }
-        __syncthreads();
-        prefix |= (uint32_t)sh.s_digit << shift;
-        pmask |= 255u << shift;
-        want = sh.s_want;
-        __syncthreads();
-    }
-    const uint32_t T = prefix;   // the K-th largest key; `want` keys equal to T are taken
-    int ngt_t = 0;
-#pragma unroll
-    for (int e = 0; e < PT; ++e) ngt_t += (key[e] > T) ? 1 : 0;
-    int ngt;
-    int p = block_excl_scan(ngt_t, sh.wsum, ngt);
-#pragma unroll
-    for (int e = 0; e < PT; ++e)
-        if (key[e] > T && p < K) sh.cand[p++] = pack_entry(key[e], id_of(e));
-    // equal keys in id order: id order is (j, thread, q)
-    int taken_base = 0;
-#pragma unroll
-    for (int j = 0; j < PT / 4; ++j) {
-        int neq = 0;
-#pragma unroll
-        for (int q2 = 0; q2 < 4; ++q2) neq += (key[4 * j + q2] == T) ? 1 : 0;
-        int tot;
-        int ord = taken_base + block_excl_scan(neq, sh.wsum, tot);
-#pragma unroll
-        for (int q2 = 0; q2 < 4; ++q2) {
-            if (key[4 * j + q2] == T) {
-                if (ord < want && ngt + ord < K) sh.cand[ngt + ord] = pack_entry(T, id_of(4 * j + q2));
-                ++ord;
-            }
-        }
-        taken_base += tot;
-    }
-    if (tid == 0) sh.cand[K] = kEmptyEntry;
-    __syncthreads();
-    rank_place(sh.cand, K, K, out);
-    __syncthreads();
-}
-
-// Number of entries of the descending list y[0..n) that are > x (strict) or
-// >= x (when `or_equal`).
-__device__ __forceinline__ int count_better(const uint64_t* y, int n, uint64_t x, bool or_equal) {
-    int lo = 0, hi = n;   // first index whose entry does not beat x
-    while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        const bool beats = or_equal ? (y[mid] >= x) : (y[mid] > x);
-        if (beats) lo = mid + 1; else hi = mid;
-    }
-    return lo;
-}
-
-// Merge nl slot-ordered lists of K entries held in LDS at a[0 .. nl K) (b is
-// scratch of the same size) pairwise into one; returns the buffer holding it.
-__device__ __forceinline__ uint64_t* merge_lists(uint64_t* a, uint64_t* b, int nl, int K) {
-    const int tid = threadIdx.x;
-    while (nl > 1) {
-        const int pairs = nl >> 1;
-        // one thread per entry of both lists of every pair
-        for (int i = tid; i < pairs * 2 * K; i += kThreads) {
-            const int pr = i / (2 * K), r = i % (2 * K);
-            const uint64_t* x = a + (int64_t)(2 * pr) * K;
-            const uint64_t* y = x + K;
-            int dst;
-            uint64_t e;
-            if (r < K) { e = x[r]; dst = r + count_better(y, K, e, false); }
-            else { e = y[r - K]; dst = (r - K) + count_better(x, K, e, true); }
-            if (dst < K) b[(int64_t)pr * K + dst] = e;
-        }
-        if (nl & 1)
-            for (int i = tid; i < K; i += kThreads) b[(int64_t)pairs * K + i] = a[(int64_t)(nl - 1) * K + i];
-        __syncthreads();
-        uint64_t* t = a; a = b; b = t;
-        nl = pairs + (nl & 1);
-    }
-    return a;
-}
-
-// Slot k of row m from the final list: draft id, target id, unary score.
-__device__ __forceinline__ void write_row(const uint64_t* list, int m, int K, int V, float lse,
-                                          const int64_t* __restrict__ d2t, int32_t* __restrict__ cand_idx,
-                                          int64_t* __restrict__ cand_tok, float* __restrict__ unary) {
-    for (int k = threadIdx.x; k < K; k += kThreads) {
-        const uint64_t e = list[k];
-        uint32_t id = entry_id(e);
-        id = min(id, (uint32_t)(V - 1));   // an empty entry cannot reach the top K when K <= V
-        const float z = key_to_float(entry_key(e));
-        const int64_t o = (int64_t)m * K + k;
-        cand_idx[o] = (int32_t)id;
-        cand_tok[o] = d2t ? (int64_t)id + d2t[id] : (int64_t)id;
-        unary[o] = z - lse;
-    }
-}
-
-// ---------------------------------------------------------------- from tile maxima
-// When the lm_head kernel also stored the maximum of every 32-logit tile of
-// every row, the top K of a row needs only a few of its tiles.  If tau is at
-// most the K-th largest tile maximum, at least K logits are >= tau, so every
-// member of the top K is >= tau and sits in a tile whose maximum is >= tau.
-// tau comes from the per-thread maxima of the tile maxima as in chunk_select;
-// the tiles it keeps (about K + 30 on smooth rows) are read, their logits
-// >= tau ranked.  A row with more than kSelCap such tiles or kCandCap such
-// logits (heavy ties) takes the exact path over all its logits instead.
-constexpr int kSelCap = 1024;
-constexpr int kCandCap = 512;
-constexpr int kTileCap = 8192;   // tile-maxima keys kept in registers (32 per thread); longer rows re-read the rest
-constexpr int kPartCap = 2048;   // lse partials loaded with the tile maxima (8 per thread); more are merged later
-
-__global__ void __launch_bounds__(kThreads) topk_tiles_kernel(const float* __restrict__ logits, int64_t ldz,
-                                                              const float* __restrict__ tmax, int64_t ldt,
-                                                              int tiles, int V, int K, int nchunks,
-                                                              const float* __restrict__ lse_in,
-                                                              const float2* __restrict__ lse_part, int nparts,
-                                                              const int64_t* __restrict__ d2t,
-                                                              int32_t* __restrict__ cand_idx,
-                                                              int64_t* __restrict__ cand_tok,
-                                                              float* __restrict__ unary) {
-    extern __shared__ uint64_t lists[];   // exact path: 2 * nchunks * K entries
-    __shared__ ChunkShared sh;
-    __shared__ int sel[kSelCap];
-    __shared__ __attribute__((aligned(16))) uint64_t cand[kCandCap + 2];
-    __shared__ uint64_t top[kMaxTopK];
-    __shared__ int s_nsel, s_ncand;
-    __shared__ float2 red[4];
-    const int tid = threadIdx.x;
-    const int m = blockIdx.x;
-    const float* row = logits + (int64_t)m * ldz;
-    const float* trow = tmax + (int64_t)m * ldt;
-    // ---- loads: the first kPartCap lse partials (or the caller's lse), then the first
-    // kTileCap tile maxima, which are still in flight while the partials are merged
-    constexpr int kTPT = kTileCap / kThreads;   // tile maxima per thread in the first round
-    constexpr int kPPT = kPartCap / kThreads;   // lse partials per thread in the first round
-    const float2* prow = lse_part ? lse_part + (int64_t)m * nparts : nullptr;
-    // Every load below is issued by every lane (indices past the end are clamped and the
-    // value replaced), so that the compiler can count the tile-maxima loads as issued after
-    // the partials and wait for the partials alone.
-    float2 pv[kPPT];
-    if (prow) {
-#pragma unroll
-        for (int i = 0; i < kPPT; ++i) {
-            const int idx = tid + kThreads * i;
-            const float2 x = prow[idx < nparts ? idx : nparts - 1];
-            pv[i] = idx < nparts ? x : make_float2(0.f, 0.f);
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < kPPT; ++i) pv[i] = make_float2(0.f, 0.f);
-    }
-    const float lse_given = lse_part ? 0.f : lse_in[m];
-    float tv[kTPT];
-#pragma unroll
-    for (int i = 0; i < kTPT; ++i) {
-        const int t = tid + kThreads * i;
-        const float x = trow[t < tiles ? t : tiles - 1];
-        tv[i] = t < tiles ? x : 0.f;
-    }
-    // The lse is merged in two halves: each wave's (max, sum exp) into red[], then the four
-    // waves after the next barrier.  The order of the merges is that of block_lse, so the
-    // value is the same bit for bit.
-    auto lse_wave = [&]() __attribute__((always_inline)) {
-        if (!prow) return;
-        float a = 0.f, sm = 0.f;
-#pragma unroll
-        for (int i = 0; i < kPPT; ++i) lse_merge(a, sm, pv[i].x, pv[i].y);
-        for (int base = kPartCap; base < nparts; base += kPartCap) {
-            float2 v[kPPT];
-#pragma unroll
-            for (int i = 0; i < kPPT; ++i) {
-                const int idx = base + tid + kThreads * i;
-                v[i] = idx < nparts ? prow[idx] : make_float2(0.f, 0.f);
-            }
-#pragma unroll
-            for (int i = 0; i < kPPT; ++i) lse_merge(a, sm, v[i].x, v[i].y);
-        }
-        for (int o = 32; o > 0; o >>= 1) {
-            const float m2 = __shfl_xor(a, o);
-            const float s2 = __shfl_xor(sm, o);
-            lse_merge(a, sm, m2, s2);
-        }
-        if ((tid & 63) == 0) red[tid >> 6] = make_float2(a, sm);
-    };
-    auto lse_final = [&]() __attribute__((always_inline)) {   // after a barrier that follows lse_wave
-        if (!prow) return lse_given;
-        float a = 0.f, sm = 0.f;
-        for (int w = 0; w < 4; ++w) lse_merge(a, sm, red[w].x, red[w].y);
-        return a + logf(sm);
-    };
-
-    lse_wave();
-
-    // ---- tau from the tile maxima; their keys stay in registers
-    uint32_t kv[kTPT];
-    uint32_t mx = 0;
-#pragma unroll
-    for (int i = 0; i < kTPT; ++i) {
-        const int t = tid + kThreads * i;
-        kv[i] = t < tiles ? float_to_key(tv[i]) : 0u;   // 0 is below every tau
-        mx = max(mx, kv[i]);
-    }
-    for (int t = kTileCap + tid; t < tiles; t += kThreads) mx = max(mx, float_to_key(trow[t]));
-    const uint32_t sorted = wave_sort_desc(mx);
-    const int q = (K + 3) >> 2;
-    const uint32_t wq = (uint32_t)__builtin_amdgcn_readlane((int)sorted, q - 1);
-    if ((tid & 63) == 0) sh.wtau[tid >> 6] = wq;
-    if (tid == 0) { s_nsel = 0; s_ncand = 0; }
-    __syncthreads();
-    const uint32_t tau = max(min(min(sh.wtau[0], sh.wtau[1]), min(sh.wtau[2], sh.wtau[3])), 1u);
-    const float lse = lse_final();
-
-    // ---- the tiles that may hold a member of the top K: a prefix count over the wave and
-    // one LDS atomic per wave place each thread's tiles in sel[]
-    {
-        int c = 0;
-#pragma unroll
-        for (int i = 0; i < kTPT; ++i) c += kv[i] >= tau ? 1 : 0;
-        const int lane = tid & 63;
-        int x = c;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const int y = __shfl_up(x, o);
-            if (lane >= o) x += y;
-        }
-        int base = 0;
-        if (lane == 63 && x > 0) base = atomicAdd(&s_nsel, x);
-        base = __shfl(base, 63);
-        int j = base + x - c;
-#pragma unroll
-        for (int i = 0; i < kTPT; ++i) {
-            if (kv[i] >= tau) {
-                if (j < kSelCap) sel[j] = tid + kThreads * i;
-                ++j;
-            }
-        }
-    }
-    for (int t = kTileCap + tid; t < tiles; t += kThreads) {
-        if (float_to_key(trow[t]) >= tau) {
-            const int j = atomicAdd(&s_nsel, 1);
-            if (j < kSelCap) sel[j] = t;
-        }
-    }
-    __syncthreads();
-    const int nsel = s_nsel;
-    bool exact = nsel > kSelCap;
-    if (!exact) {
-        // ---- their logits >= tau (sixteen loads in flight per thread at a time: one round
-        // for up to 128 tiles)
-        float zv[16];
-        auto load_round = [&](int base) __attribute__((always_inline)) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int e = base + tid + kThreads * i;
-                const int v = e < nsel * 32 ? sel[e >> 5] * 32 + (e & 31) : V;
-                zv[i] = v < V ? row[v] : 0.f;
-            }
-        };
-        auto scan_round = [&](int base) __attribute__((always_inline)) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int e = base + tid + kThreads * i;
-                const int v = e < nsel * 32 ? sel[e >> 5] * 32 + (e & 31) : V;
-                if (v < V) {
-                    const uint32_t k = float_to_key(zv[i]);
-                    if (k >= tau) {
-                        const int c = atomicAdd(&s_ncand, 1);
-                        if (c < kCandCap) cand[c] = pack_entry(k, (uint32_t)v);
-                    }
-                }
-            }
-        };
-        for (int base = 0; base < nsel * 32; base += kThreads * 16) {
-            load_round(base);
-            scan_round(base);
-        }
-        __syncthreads();
-        const int n = s_ncand;
-        exact = n > kCandCap;
-        if (!exact) {
-            if (tid == 0) cand[n] = kEmptyEntry;
-            __syncthreads();
-            rank_place(cand, n, K, top);
-            __syncthreads();
-            write_row(top, m, K, V, lse, d2t, cand_idx, cand_tok, unary);
-            return;
-        }
-    }
-    // ---- exact path: every chunk of the row, then the merge, all in this workgroup
-    for (int c = 0; c < nchunks; ++c) chunk_select<64>(row, c * (kThreads * 64), V, K, lists + (int64_t)c * K, sh);
-    const uint64_t* fin = merge_lists(lists, lists + (int64_t)nchunks * K, nchunks, K);
-    write_row(fin, m, K, V, lse, d2t, cand_idx, cand_tok, unary);
+__global__ void __launch_bounds__(kThreads) topk_tiles_kernel(TopkRowArgs a) {
+    __shared__ TopkSmem s;
+    topk_row(a, blockIdx.x, s);
 }
 
 }  // namespace
@@ -610,16 +147,15 @@ hipError_t launch_argmax(const float* logits, int64_t ldz, const float* tile_max
     return hipGetLastError();
 }
 
-int topk_tiles_chunks(int V) { return (V + kThreads * 64 - 1) / (kThreads * 64); }
+int topk_tiles_chunks(int V) { return topk_chunks(V); }
 
 hipError_t launch_topk_tiles(const float* logits, int64_t ldz, const float* tile_max, int64_t ldt,
                              const float* lse, const float2* lse_part, int nparts, const int64_t* d2t, int M, int V,
                              int K, int32_t* cand_idx, int64_t* cand_tok, float* unary, hipStream_t s) {
     if (M <= 0) return hipSuccess;
-    const int nchunks = topk_tiles_chunks(V);
-    const size_t lds = (size_t)2 * nchunks * K * sizeof(uint64_t);
-    hipLaunchKernelGGL(topk_tiles_kernel, dim3(M), dim3(kThreads), lds, s, logits, ldz, tile_max, ldt,
-                       (V + 31) / 32, V, K, nchunks, lse, lse_part, nparts, d2t, cand_idx, cand_tok, unary);
+    const TopkRowArgs a = topk_row_args(logits, ldz, tile_max, ldt, lse, lse_part, nparts, d2t, V, K, cand_idx,
+                                        cand_tok, unary);
+    hipLaunchKernelGGL(topk_tiles_kernel, dim3(M), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 
