@@ -168,6 +168,13 @@ class Workload:
                              gate_w=self.gate_w, block_len=s.L, walk=self.walk, workspace=self.ws,
                              out=(self.tokens, self.scores))
 
+    def step_filtered(self):
+        """The step with the opt-in logits filter (DFLASH_OPT_FILTER_LOGITS)."""
+        s = self.shape
+        self.api.draft_block(self.hidden, self.W, self.tables, self.last_tok, top_k=s.K, d2t=self.d2t,
+                             gate_w=self.gate_w, block_len=s.L, walk=self.walk, workspace=self.ws,
+                             out=(self.tokens, self.scores), filter_logits=True)
+
     def lm_head(self, zbuf):
         return lambda: self.api.lm_head(self.hidden, self.W, workspace=self.ws, with_lse=False, out=zbuf)
 
@@ -191,6 +198,7 @@ def workload_entry(w, timer, args):
     cold = stats(timer.per_iter(w.step, args.iters, warm=2, cold=True))
     zbuf = w.torch.empty((s.M, w.api.logits_stride(s.Vd)), dtype=w.torch.float32, device="cuda")
     lm = stats(timer.per_iter(w.lm_head(zbuf), args.iters, warm=3))
+    filt = stats(timer.per_iter(w.step_filtered, args.iters, warm=3))
     del zbuf
     b = step_bytes(s)
     t = warm["median_us"] * 1e-6
@@ -206,6 +214,8 @@ def workload_entry(w, timer, args):
                      "as_architected_bytes": b["as_architected"], "as_architected_us": round(arch_s * 1e6, 2),
                      "frac_of_as_architected": round(arch_s / t, 4)},
         "lm_head_alone": lm,
+        "step_with_logits_filter": {**filt, "note": "opt-in DFLASH_OPT_FILTER_LOGITS: sample GEMM + bound + "
+                                    "filtered lm_head; same tokens"},
         "lm_head_gbs": round(b["lm_head"] / (lm["mean_us"] * 1e-6) / 1e9, 1),
         "lm_head_mfma_tflops": round(2.0 * s.M * s.H * s.Vd / (lm["mean_us"] * 1e-6) / 1e12, 1),
     }
@@ -394,6 +404,7 @@ def main():
                    "host_enqueue_us_per_step": round(host_us, 1),
                    "cold_flush": "1 GiB read-modify-write before every iteration, outside the events"},
         "step_roofline": main_entry["roofline"],
+        "step_with_logits_filter": main_entry["step_with_logits_filter"],
         "standalone_topk_pass": {"achieved_gbs": round(k2_gbs, 1), "frac": round(k2_gbs / HBM_PEAK_GBS, 4),
                                  "bytes_per_launch": k2_bytes, "cold": k2c, "warm": k2,
                                  "graded_on": "cold median"},

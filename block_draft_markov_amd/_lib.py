@@ -12,6 +12,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdflash_d
 
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, -1, -2, -3, -4
 WALK_VITERBI, WALK_GREEDY = 0, 1
+OPT_FILTER_LOGITS = 1
 MAX_TOP_K, MAX_BLOCK_LEN = 64, 100
 LATTICE_NOALLOC_MAX_BYTES = 16 << 20
 
@@ -33,6 +34,7 @@ class Dims(ctypes.Structure):
         ("top_k", _I32),
         ("rank", _I32),
         ("walk", _I32),
+        ("options", _I32),
     ]
 
 

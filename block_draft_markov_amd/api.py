@@ -17,7 +17,7 @@ from typing import Optional, Sequence, Tuple
 
 import torch
 
-from ._lib import (DFlashError, Dims, MAX_BLOCK_LEN, WALK_GREEDY, WALK_VITERBI, check, load)
+from ._lib import (DFlashError, Dims, MAX_BLOCK_LEN, OPT_FILTER_LOGITS, WALK_GREEDY, WALK_VITERBI, check, load)
 
 __all__ = ["Dims", "DFlashError", "make_dims", "workspace_bytes", "logits_stride", "draft_block",
            "draft_block_sampled", "draft_argmax", "draft_dense", "lm_head", "row_lse", "topk", "pair_scores",
@@ -33,11 +33,11 @@ _F64 = (torch.float64,)
 
 
 def make_dims(*, R: int, L: int, M: int, H: int, Vd: int, Vt: Optional[int] = None, K: int, r: int = 1,
-              walk="viterbi") -> Dims:
+              walk="viterbi", filter_logits: bool = False) -> Dims:
     if walk not in _WALKS:
         raise ValueError(f"walk must be 'viterbi' or 'greedy', got {walk!r}")
     return Dims(int(R), int(L), int(M), int(H), int(Vd), int(Vd if Vt is None else Vt), int(K), int(r),
-                _WALKS[walk])
+                _WALKS[walk], OPT_FILTER_LOGITS if filter_logits else 0)
 
 
 def workspace_bytes(d: Dims) -> int:
@@ -200,8 +200,9 @@ def _lattice_args(hidden, lm_head_w, tables, last_tok, d2t, gate_w, row_offsets)
 def draft_block(hidden: torch.Tensor, lm_head_w: torch.Tensor, tables: torch.Tensor, last_tok: torch.Tensor, *,
                 top_k: int, d2t: Optional[torch.Tensor] = None, gate_w: Optional[torch.Tensor] = None,
                 row_offsets: Optional[torch.Tensor] = None, block_len: Optional[int] = None, walk="viterbi",
-                workspace: Optional[Workspace] = None, out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None):
-    """The whole draft step: (tokens int64 [M], scores fp32 [R])."""
+                workspace: Optional[Workspace] = None, out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None,
+                filter_logits: bool = False):
+    """The whole draft step: (tokens int64 [M], scores fp32 [R]).  filter_logits: DFLASH_OPT_FILTER_LOGITS."""
     M, H, Vd, Vt, r, R = _lattice_args(hidden, lm_head_w, tables, last_tok, d2t, gate_w, row_offsets)
     dev = hidden.device
     tokens, scores = _outs(out, dev, [("tokens", _I64, (M,), False), ("scores", _F32, (R,), False)])
@@ -209,7 +210,7 @@ def draft_block(hidden: torch.Tensor, lm_head_w: torch.Tensor, tables: torch.Ten
     _check_block_len(L)
     _on_device(dev, lm_head=lm_head_w, tables=tables, last_tok=last_tok, d2t=d2t, gate_w=gate_w,
                row_offsets=row_offsets)
-    d = make_dims(R=R, L=L, M=M, H=H, Vd=Vd, Vt=Vt, K=top_k, r=r, walk=walk)
+    d = make_dims(R=R, L=L, M=M, H=H, Vd=Vd, Vt=Vt, K=top_k, r=r, walk=walk, filter_logits=filter_logits)
     wsp, wsn = _ws(workspace, dev).get(workspace_bytes(d))
     check(load().dflash_draft_block(ctypes.byref(d), _ptr(hidden), _ptr(lm_head_w), _ptr(d2t), _ptr(tables),
                                     _ptr(gate_w), _ptr(last_tok), _ptr(row_offsets), _ptr(tokens), _ptr(scores),
@@ -221,7 +222,7 @@ def draft_block_sampled(hidden: torch.Tensor, lm_head_w: torch.Tensor, tables: t
                         last_tok: torch.Tensor, uniforms: torch.Tensor, *, top_k: int, temperature: float = 1.0,
                         d2t: Optional[torch.Tensor] = None, gate_w: Optional[torch.Tensor] = None,
                         row_offsets: Optional[torch.Tensor] = None, block_len: Optional[int] = None,
-                        workspace: Optional[Workspace] = None, with_q: bool = True):
+                        workspace: Optional[Workspace] = None, with_q: bool = True, filter_logits: bool = False):
     """The whole step with the sampled walk: (tokens int64 [M], scores fp32 [R], q float64 [M, K] or None)."""
     M, H, Vd, Vt, r, R = _lattice_args(hidden, lm_head_w, tables, last_tok, d2t, gate_w, row_offsets)
     _arg(uniforms, "uniforms", _F64, (M,))
@@ -230,7 +231,7 @@ def draft_block_sampled(hidden: torch.Tensor, lm_head_w: torch.Tensor, tables: t
     _check_block_len(L)
     _on_device(dev, lm_head=lm_head_w, tables=tables, last_tok=last_tok, d2t=d2t, gate_w=gate_w,
                row_offsets=row_offsets, uniforms=uniforms)
-    d = make_dims(R=R, L=L, M=M, H=H, Vd=Vd, Vt=Vt, K=top_k, r=r)
+    d = make_dims(R=R, L=L, M=M, H=H, Vd=Vd, Vt=Vt, K=top_k, r=r, filter_logits=filter_logits)
     tokens = torch.empty(M, dtype=torch.int64, device=dev)
     scores = torch.empty(R, dtype=torch.float32, device=dev)
     q = torch.empty((M, top_k), dtype=torch.float64, device=dev) if with_q else None

@@ -71,6 +71,8 @@ int check_dims(const dflash_dims* d) {
         return fail(DFLASH_EINVAL, "rank = %d outside [1, %lld]", d->rank, (long long)kMaxRank);
     if (d->walk != DFLASH_WALK_VITERBI && d->walk != DFLASH_WALK_GREEDY)
         return fail(DFLASH_EINVAL, "walk = %d is neither DFLASH_WALK_VITERBI nor DFLASH_WALK_GREEDY", d->walk);
+    if (d->options & ~DFLASH_OPT_FILTER_LOGITS)
+        return fail(DFLASH_EINVAL, "options = %d has bits other than DFLASH_OPT_FILTER_LOGITS", d->options);
     if ((int64_t)dflash::topk_tiles_chunks(d->draft_vocab) * d->top_k > 2048)
         return fail(DFLASH_EUNSUPPORTED, "draft_vocab = %d is too large for top_k = %d", d->draft_vocab, d->top_k);
     return DFLASH_OK;
@@ -93,8 +95,9 @@ int need(const void* p, int64_t count, const char* name) {
 struct Layout {
     int64_t ldz;
     int64_t ldt;      // tile maxima stride (0: none, the Top-K reads every logit)
-    size_t logits, lse, part, tmax, cidx, ctok, unary, pair, dense, total;
+    size_t logits, lse, part, tmax, cidx, ctok, unary, pair, dense, zs, tau, tmask, total;
     int nparts;
+    int sample;       // vocabulary tiles sampled for the lm_head's logits filter (0: no filter)
 };
 
 Layout layout(const dflash_dims* d) {
@@ -118,6 +121,11 @@ Layout layout(const dflash_dims* d) {
     l.unary = take((size_t)(M * K) * sizeof(float));
     l.pair = take((size_t)(M * K * K) * sizeof(float));
     l.dense = take((size_t)((int64_t)d->num_requests * d->block_len) * sizeof(uint64_t));
+    l.sample = (d->options & DFLASH_OPT_FILTER_LOGITS) ? dflash::lmhead_sample_tiles(d->total_rows, d->draft_vocab)
+                                                        : 0;
+    l.zs = take((size_t)(M * 32 * l.sample) * sizeof(float));
+    l.tau = take((size_t)(l.sample ? M : 0) * sizeof(float));
+    l.tmask = take((size_t)(l.sample ? M * l.ldt : 0));
     l.total = off > 0 ? off : 256;
     return l;
 }
@@ -167,16 +175,34 @@ int whole_step(const dflash_dims* d, const uint16_t* hidden, const uint16_t* lm_
     float* logits = at<float>(ws, l.logits);
     float2* part = at<float2>(ws, l.part);
     float* tmax = at<float>(ws, l.tmax);
+    // Logits filter (large batches): the exact logits of a sample of vocabulary tiles give
+    // each row a bound tau at most its K-th largest logit; the lm_head kernel then writes only
+    // the groups of four logits that reach tau (and a mask of them), and the Top-K reads only
+    // those.  Every member of the top K is at least tau, so the slots are those of the
+    // unfiltered logits.
+    float* tau = nullptr;
+    uint8_t* tmask = nullptr;
+    if (l.sample > 0) {
+        tau = at<float>(ws, l.tau);
+        tmask = at<uint8_t>(ws, l.tmask);
+        float* zs = at<float>(ws, l.zs);
+        const int64_t ldzs = (int64_t)32 * l.sample;
+        if ((e = dflash::launch_lmhead_sample(hidden, lm_head, d->total_rows, d->hidden, d->draft_vocab, l.sample,
+                                              zs, ldzs, s)) != hipSuccess)
+            return hip_fail(e, "lm_head sample launch");
+        if ((e = dflash::launch_sample_tau(zs, ldzs, (int)ldzs, d->total_rows, d->top_k, tau, s)) != hipSuccess)
+            return hip_fail(e, "sample bound launch");
+    }
     // the lm_head kernel stores the tile maxima (there are some whenever there are rows)
     if ((e = dflash::launch_lmhead(hidden, lm_head, logits, l.ldz, part, tmax, l.ldt, d->total_rows, d->hidden,
-                                   d->draft_vocab, s)) != hipSuccess)
+                                   d->draft_vocab, s, tau, tmask)) != hipSuccess)
         return hip_fail(e, "lm_head launch");
     int32_t* cidx = at<int32_t>(ws, l.cidx);
     int64_t* ctok = at<int64_t>(ws, l.ctok);
     float* unary = at<float>(ws, l.unary);
     float* pair = at<float>(ws, l.pair);
     if ((e = dflash::launch_topk_tiles(logits, l.ldz, tmax, l.ldt, nullptr, part, l.nparts, d2t, d->total_rows,
-                                       d->draft_vocab, d->top_k, cidx, ctok, unary, s)) != hipSuccess)
+                                       d->draft_vocab, d->top_k, cidx, ctok, unary, s, tmask, tau)) != hipSuccess)
         return hip_fail(e, "top-k launch");
     if ((e = dflash::launch_pair_scores(ctok, tables, gate_w, hidden, last_tok, row_offsets, d->num_requests,
                                         d->block_len, d->total_rows, d->hidden, d->target_vocab, d->top_k, d->rank,

@@ -14,8 +14,21 @@ int lmhead_partials(int M, int V);       // (max, sum exp) partials per row
 // The kernel can also store the maximum of every tile of 32 logits of every
 // row: tile_max [M][ldt], ldt >= ceil(V / 32).
 bool lmhead_has_tile_max(int M);
+// With tau (a per-row lower bound of the K-th largest logit) and tile_mask, a kernel of
+// more than 64 rows writes only the groups of four logits whose maximum reaches tau and
+// records them in tile_mask [M][ldt] (bit q of a tile's byte: logits 4 q .. 4 q + 3 of the
+// tile written); the partly filled last tile is written whole.
 hipError_t launch_lmhead(const uint16_t* hidden, const uint16_t* W, float* logits, int64_t ldz,
-                         float2* lse_part, float* tile_max, int64_t ldt, int M, int H, int V, hipStream_t s);
+                         float2* lse_part, float* tile_max, int64_t ldt, int M, int H, int V, hipStream_t s,
+                         const float* tau = nullptr, uint8_t* tile_mask = nullptr);
+// Vocabulary tiles sampled for tau (0: no filtered kernel for this shape: at most 64 rows, or
+// fewer than 512 tiles), and the sample:
+// zs [M][ldzs], ldzs >= 32 S, the exact logits of the sampled tiles.
+int lmhead_sample_tiles(int M, int V);
+hipError_t launch_lmhead_sample(const uint16_t* hidden, const uint16_t* W, int M, int H, int V, int S, float* zs,
+                                int64_t ldzs, hipStream_t s);
+// tau[m] = the K-th largest of the n sample logits of row m (n <= 4096).
+hipError_t launch_sample_tau(const float* zs, int64_t ldzs, int n, int M, int K, float* tau, hipStream_t s);
 // lse[m] from the partials of row m.
 hipError_t launch_lse_combine(const float2* lse_part, int nparts, float* lse, int M, hipStream_t s);
 // lse[m] straight from logits.
@@ -28,9 +41,12 @@ int topk_tiles_chunks(int V);
 // Top-K from the maxima of the 32-logit tiles (one workgroup per row; rows with
 // heavy ties take an exact path over all their logits in the same launch).  The lse
 // of a row is lse[m] when lse is given, else merged from its (max, sum exp) partials.
+// With tile_mask and tau (from the filtered lm_head kernel) only the written groups of
+// logits are read, and tau raises the row's threshold.
 hipError_t launch_topk_tiles(const float* logits, int64_t ldz, const float* tile_max, int64_t ldt,
                              const float* lse, const float2* lse_part, int nparts, const int64_t* d2t, int M,
-                             int V, int K, int32_t* cand_idx, int64_t* cand_tok, float* unary, hipStream_t s);
+                             int V, int K, int32_t* cand_idx, int64_t* cand_tok, float* unary, hipStream_t s,
+                             const uint8_t* tile_mask = nullptr, const float* tau = nullptr);
 // tile_max [M][ldt]: the maximum of every 32-logit tile of every row of logits [M][ldz].
 hipError_t launch_tile_max(const float* logits, int64_t ldz, int M, int V, float* tile_max, int64_t ldt,
                            hipStream_t s);

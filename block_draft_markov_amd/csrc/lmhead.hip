@@ -43,6 +43,8 @@ struct LmHeadArgs {
     int M, H, V;
     int tiles;   // vocab tiles: ceil(V / 32)
     int G;       // workgroups along the vocabulary
+    const float* tau;   // per-row lower bound of the K-th largest logit (filtered kernel only)
+    uint8_t* tmask;     // [M][ldt]: groups of four logits written per tile (filtered kernel only)
 };
 
 template <int I, int N, class F>
@@ -123,7 +125,7 @@ __device__ __forceinline__ void dma16(u32x4 rsrc, uint32_t lds, int voff, int so
 
 constexpr int kNV = 2;                    // vocab tiles per wave and pass (more than 64 rows)
 constexpr int kWSlots = 3;                // W slots per wave: W runs kWSlots - 1 steps ahead
-template <int MT, bool HFULL, int NVT, int SW = kWSlots>
+template <int MT, bool HFULL, int NVT, int SW = kWSlots, bool FILTER = false>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 lmhead_dma_kernel(LmHeadArgs a) {
     static_assert(SW >= 3, "the wait before each barrier assumes W is issued two or more steps ahead");
@@ -248,6 +250,14 @@ lmhead_dma_kernel(LmHeadArgs a) {
     float run_m[MT], run_s[MT];     // running (max, sum exp) of the lane's half of its rows
 #pragma unroll
     for (int i = 0; i < MT; ++i) { run_m[i] = -INFINITY; run_s[i] = 0.f; }
+    // FILTER: a group of four logits is written only when its maximum reaches the row's
+    // bound tau (at most the row's K-th largest logit, so no member of the top K is left out)
+    float tau_r[FILTER ? MT : 1];
+#pragma unroll
+    for (int i = 0; i < (FILTER ? MT : 1); ++i) {
+        const int m = m0 + i * 32 + lr;
+        tau_r[i] = FILTER && m < a.M ? a.tau[m] : -INFINITY;
+    }
 
     // ---- MFMAs of one step for NA tiles: W fragments first, then batch tiles, reads one tile ahead
     auto mfma_step = [&](auto& acc, uint32_t hs, uint32_t ws) __attribute__((always_inline)) {
@@ -313,14 +323,25 @@ lmhead_dma_kernel(LmHeadArgs a) {
                         for (int j = 0; j < 16; ++j)
                             if (col + 8 * (j >> 2) + (j & 3) >= a.V) z[j] = -INFINITY;
                     }
+                    uint32_t bits = 0;   // FILTER: groups 2 g + lh of the tile this lane wrote
                     if (m < a.M) {
                         float* dst = a.logits + (int64_t)m * a.ldz + col;
                         if (full) {
 #pragma unroll
-                            for (int g = 0; g < 4; ++g)
-                                *reinterpret_cast<f32x4*>(dst + 8 * g) =
-                                    f32x4{z[4 * g], z[4 * g + 1], z[4 * g + 2], z[4 * g + 3]};
+                            for (int g = 0; g < 4; ++g) {
+                                bool put = true;
+                                if constexpr (FILTER) {
+                                    const float gm = fmaxf(fmaxf(z[4 * g], z[4 * g + 1]),
+                                                           fmaxf(z[4 * g + 2], z[4 * g + 3]));
+                                    put = gm >= tau_r[i];
+                                    bits |= put ? 1u << (2 * g + lh) : 0u;
+                                }
+                                if (put)
+                                    *reinterpret_cast<f32x4*>(dst + 8 * g) =
+                                        f32x4{z[4 * g], z[4 * g + 1], z[4 * g + 2], z[4 * g + 3]};
+                            }
                         } else {
+                            bits = 0xFFu;   // the partly filled last tile is written whole
 #pragma unroll
                             for (int j = 0; j < 16; ++j)
                                 if (col + 8 * (j >> 2) + (j & 3) < a.V) dst[8 * (j >> 2) + (j & 3)] = z[j];
@@ -336,6 +357,10 @@ lmhead_dma_kernel(LmHeadArgs a) {
                                                                           false, false);
                         const float tm = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
                         if (lh == 0 && m < a.M) a.tmax[(int64_t)m * a.ldt + tile] = tm;
+                        if constexpr (FILTER) {
+                            const auto sb = __builtin_amdgcn_permlane32_swap(bits, bits, false, false);
+                            if (lh == 0 && m < a.M) a.tmask[(int64_t)m * a.ldt + tile] = (uint8_t)(sb[0] | sb[1]);
+                        }
                     }
                     const float nm = fmaxf(run_m[i], mx);
                     if (full || nm != -INFINITY) {
@@ -414,6 +439,15 @@ lmhead_dma_kernel(LmHeadArgs a) {
 
 template <int MT, int NV>
 hipError_t launch_rows(const LmHeadArgs& a, dim3 grid, hipStream_t s) {
+    if constexpr (NV > 1) {
+        if (a.tau) {
+            if (a.H % kBK == 0)
+                hipLaunchKernelGGL((lmhead_dma_kernel<MT, true, NV, kWSlots, true>), grid, dim3(256), 0, s, a);
+            else
+                hipLaunchKernelGGL((lmhead_dma_kernel<MT, false, NV, kWSlots, true>), grid, dim3(256), 0, s, a);
+            return hipGetLastError();
+        }
+    }
     if (a.H % kBK == 0)
         hipLaunchKernelGGL((lmhead_dma_kernel<MT, true, NV>), grid, dim3(256), 0, s, a);
     else
@@ -437,6 +471,66 @@ int lmhead_grid(int M, int V) {
     const int need = (tiles + per_pass - 1) / per_pass;
     const int cap = 256 / row_chunks(M) > 0 ? 256 / row_chunks(M) : 1;
     return need < cap ? need : cap;
+}
+
+// ---------------------------------------------------------------- the sample of the filter
+// The exact logits of S vocabulary tiles (tile floor(j T / S) for j < S, T tiles; all
+// full when T >= 4 S) for every row, by the same MFMA sequence as lmhead_dma_kernel: for
+// each 64-wide step ks and sub-step s, lane l of the wave feeds W row l % 32 and batch
+// row l % 32 with reduction indices 64 ks + 32 (l / 32) + 8 s .. + 7 (zero past H), into
+// one accumulator per 32 x 32 tile, in that order.  So every sample logit equals the
+// main kernel's logit of the same row and vocabulary id bit for bit, and the K-th
+// largest sample logit of a row is at most the row's K-th largest logit.
+// One wave per (sampled tile, 32-row batch tile); fragments come straight from memory.
+constexpr int kSampleTiles = 128;
+__global__ void __launch_bounds__(64) lmhead_sample_kernel(const uint16_t* __restrict__ hidden,
+                                                           const uint16_t* __restrict__ W, int M, int H,
+                                                           int tiles, int S, float* __restrict__ zs,
+                                                           int64_t ldzs) {
+    const int j = blockIdx.x, i = blockIdx.y;
+    const int lane = threadIdx.x, lr = lane & 31, lh = lane >> 5;
+    const int t = (int)((int64_t)j * tiles / S);
+    const int mrow = i * 32 + lr;
+    const bool hrow = mrow < M;
+    const bf16x8* wp = reinterpret_cast<const bf16x8*>(W + ((int64_t)t * 32 + lr) * H);
+    const bf16x8* hp = reinterpret_cast<const bf16x8*>(hidden + (int64_t)(hrow ? mrow : 0) * H);
+    const int hchunks = H / 8, nks = (H + kBK - 1) / kBK;
+    const bf16x8 zero = {};
+    f32x16 acc = f32x16{};
+    // a ring of kRing steps of fragments in registers: the loads of step ks + kRing are issued
+    // as soon as step ks has been multiplied, so the one accumulator chain never waits for
+    // more than the latency of a load spread over kRing steps
+    constexpr int kRing = 8;
+    bf16x8 wf[kRing][4], hf[kRing][4];
+    auto load = [&](int ks, bf16x8 (&w)[4], bf16x8 (&h)[4]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int c = 8 * ks + 4 * lh + s;       // 16-byte chunk of the row
+            const bool ok = ks < nks && c < hchunks;
+            w[s] = ok ? wp[c] : zero;
+            h[s] = ok && hrow ? hp[c] : zero;
+        }
+    };
+#pragma unroll
+    for (int u = 0; u < kRing; ++u) load(u, wf[u], hf[u]);
+    for (int k0 = 0; k0 < nks; k0 += kRing) {
+#pragma unroll
+        for (int u = 0; u < kRing; ++u) {
+            if (k0 + u < nks) {
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[u][s], hf[u][s], acc, 0, 0, 0);
+                load(k0 + u + kRing, wf[u], hf[u]);
+            }
+        }
+    }
+    // register r of lane l: vocabulary entry 8 (r / 4) + 4 (l / 32) + r % 4 of the tile, batch row l % 32
+    if (hrow) {
+        float* dst = zs + (int64_t)mrow * ldzs + j * 32 + 4 * lh;
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+            *reinterpret_cast<f32x4*>(dst + 8 * g) = f32x4{acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
+    }
 }
 
 // One (max, sum) partial per row and vocabulary workgroup (or wave) -> lse.
@@ -474,14 +568,31 @@ __global__ void __launch_bounds__(256) row_lse_kernel(const float* logits, int64
 
 int lmhead_partials(int M, int V) { return lmhead_grid(M, V) * kRowsWaves; }
 
+int lmhead_sample_tiles(int M, int V) {
+    const int tiles = (V + 31) / 32;
+    return vocab_tiles_per_wave(M) > 1 && tiles >= 4 * kSampleTiles ? kSampleTiles : 0;
+}
+
+hipError_t launch_lmhead_sample(const uint16_t* hidden, const uint16_t* W, int M, int H, int V, int S, float* zs,
+                                int64_t ldzs, hipStream_t s) {
+    if (M <= 0 || S <= 0) return hipSuccess;
+    hipLaunchKernelGGL(lmhead_sample_kernel, dim3(S, (M + 31) / 32), dim3(64), 0, s, hidden, W, M, H, (V + 31) / 32,
+                       S, zs, ldzs);
+    return hipGetLastError();
+}
+
 bool lmhead_has_tile_max(int M) { return M > 0; }
 
 hipError_t launch_lmhead(const uint16_t* hidden, const uint16_t* W, float* logits, int64_t ldz,
-                         float2* lse_part, float* tile_max, int64_t ldt, int M, int H, int V, hipStream_t s) {
+                         float2* lse_part, float* tile_max, int64_t ldt, int M, int H, int V, hipStream_t s,
+                         const float* tau, uint8_t* tile_mask) {
     if (M <= 0) return hipSuccess;
     LmHeadArgs a;
     a.hidden = hidden; a.W = W; a.logits = logits; a.part = lse_part; a.ldz = ldz;
     a.tmax = tile_max; a.ldt = ldt;
+    // the filtered kernel needs tile maxima and masks, and runs only for more than 64 rows
+    a.tau = tau && tile_max && tile_mask && vocab_tiles_per_wave(M) > 1 ? tau : nullptr;
+    a.tmask = tile_mask;
     a.M = M; a.H = H; a.V = V;
     a.G = lmhead_grid(M, V);
     a.tiles = (V + 31) / 32;

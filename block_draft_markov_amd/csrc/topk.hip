@@ -17,6 +17,17 @@ __global__ void __launch_bounds__(kThreads) topk_tiles_kernel(TopkRowArgs a) {
     topk_row(a, blockIdx.x, s);
 }
 
+// The bound of the lm_head's logits filter: tau[m] = the K-th largest of the n sample logits
+// of row m (the exact logits of sampled vocabulary tiles), the last slot of their top K.
+__global__ void __launch_bounds__(kThreads) sample_tau_kernel(const float* __restrict__ zs, int64_t ldzs, int n,
+                                                              int K, float* __restrict__ tau) {
+    __shared__ ChunkShared sh;
+    __shared__ uint64_t top[kMaxTopK];
+    const int m = blockIdx.x;
+    chunk_select<16>(zs + (int64_t)m * ldzs, 0, n, K, top, sh);
+    if (threadIdx.x == 0) tau[m] = key_to_float(entry_key(top[K - 1]));
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------- head-less argmax
@@ -149,12 +160,20 @@ hipError_t launch_argmax(const float* logits, int64_t ldz, const float* tile_max
 
 int topk_tiles_chunks(int V) { return topk_chunks(V); }
 
+hipError_t launch_sample_tau(const float* zs, int64_t ldzs, int n, int M, int K, float* tau, hipStream_t s) {
+    if (M <= 0) return hipSuccess;
+    if (n > kThreads * 16 || n < K || (n & 3)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(sample_tau_kernel, dim3(M), dim3(kThreads), 0, s, zs, ldzs, n, K, tau);
+    return hipGetLastError();
+}
+
 hipError_t launch_topk_tiles(const float* logits, int64_t ldz, const float* tile_max, int64_t ldt,
                              const float* lse, const float2* lse_part, int nparts, const int64_t* d2t, int M, int V,
-                             int K, int32_t* cand_idx, int64_t* cand_tok, float* unary, hipStream_t s) {
+                             int K, int32_t* cand_idx, int64_t* cand_tok, float* unary, hipStream_t s,
+                             const uint8_t* tile_mask, const float* tau) {
     if (M <= 0) return hipSuccess;
     const TopkRowArgs a = topk_row_args(logits, ldz, tile_max, ldt, lse, lse_part, nparts, d2t, V, K, cand_idx,
-                                        cand_tok, unary);
+                                        cand_tok, unary, tile_mask, tau);
     hipLaunchKernelGGL(topk_tiles_kernel, dim3(M), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }

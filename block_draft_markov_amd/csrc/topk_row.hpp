@@ -125,9 +125,11 @@ struct ChunkShared {
 
 // The K best entries of logits [cbase, cbase + 256 PT) of `row` (ids < V), slot
 // ordered, into out[0..K) (global or LDS).  Called by all 256 threads; uses sh.
+// mask (or NULL): bit (v / 4) % 8 of byte v / 32 tells whether logits v .. v + 3 (v % 4 == 0)
+// were written; unwritten groups count as empty.
 template <int PT>
 __device__ __forceinline__ void chunk_select(const float* __restrict__ row, int cbase, int V, int K,
-                                             uint64_t* out, ChunkShared& sh) {
+                                             uint64_t* out, ChunkShared& sh, const uint8_t* mask = nullptr) {
     const int tid = threadIdx.x;
 
     // ---- load PT logits per thread: element (j, q) has id cbase + j*1024 + 4*tid + q
@@ -136,9 +138,13 @@ __device__ __forceinline__ void chunk_select(const float* __restrict__ row, int 
     for (int j = 0; j < PT / 4; ++j) {
         const int v = cbase + j * (4 * kThreads) + 4 * tid;
         f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        if (v < V) z = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + v));
+        bool put = v < V;
+        if (put) {
+            z = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + v));
+            if (mask) put = (mask[v >> 5] >> ((v >> 2) & 7)) & 1;
+        }
 #pragma unroll
-        for (int q = 0; q < 4; ++q) key[4 * j + q] = (v + q < V) ? float_to_key(z[q]) : 0u;
+        for (int q = 0; q < 4; ++q) key[4 * j + q] = (put && v + q < V) ? float_to_key(z[q]) : 0u;
     }
     auto id_of = [&](int e) { return (uint32_t)(cbase + (e >> 2) * (4 * kThreads) + 4 * tid + (e & 3)); };
 
@@ -316,18 +322,22 @@ struct TopkRowArgs {
     int32_t* cand_idx;
     int64_t* cand_tok;
     float* unary;
+    const uint8_t* tmask;   // [M][ldt] groups of the tile written, or null (every logit written)
+    const float* tau;       // [M] lower bound of the row's K-th largest logit, or null
 };
 
 __host__ __device__ inline int topk_chunks(int V) { return (V + kThreads * 64 - 1) / (kThreads * 64); }
 
 inline TopkRowArgs topk_row_args(const float* logits, int64_t ldz, const float* tmax, int64_t ldt, const float* lse,
                                  const float2* lse_part, int nparts, const int64_t* d2t, int V, int K,
-                                 int32_t* cand_idx, int64_t* cand_tok, float* unary) {
+                                 int32_t* cand_idx, int64_t* cand_tok, float* unary,
+                                 const uint8_t* tmask = nullptr, const float* tau = nullptr) {
     TopkRowArgs a;
     a.logits = logits; a.ldz = ldz; a.tmax = tmax; a.ldt = ldt;
     a.tiles = (V + 31) / 32; a.V = V; a.K = K; a.nchunks = topk_chunks(V);
     a.lse_in = lse; a.lse_part = lse_part; a.nparts = nparts; a.d2t = d2t;
     a.cand_idx = cand_idx; a.cand_tok = cand_tok; a.unary = unary;
+    a.tmask = tmask; a.tau = tmask ? tau : nullptr;
     return a;
 }
 
@@ -438,8 +448,13 @@ __device__ __forceinline__ void topk_row(const TopkRowArgs& a, int m, TopkSmem& 
     if ((tid & 63) == 0) s.sh.wtau[tid >> 6] = wq;
     if (tid == 0) { s.s_nsel = 0; s.s_ncand = 0; }
     __syncthreads();
-    const uint32_t tau = max(min(min(s.sh.wtau[0], s.sh.wtau[1]), min(s.sh.wtau[2], s.sh.wtau[3])), 1u);
+    uint32_t tau = max(min(min(s.sh.wtau[0], s.sh.wtau[1]), min(s.sh.wtau[2], s.sh.wtau[3])), 1u);
+    // the lm_head's bound also has at least K logits at or above it (it is at most the K-th
+    // largest), and every group of logits reaching it was written: the larger of the two
+    // thresholds keeps the reads to written groups
+    if (a.tau) tau = max(tau, float_to_key(a.tau[m]));
     const float lse = lse_final();
+    const uint8_t* mrow = a.tmask ? a.tmask + (int64_t)m * ldt : nullptr;
 
     // ---- the tiles that may hold a member of the top K: a prefix count over the wave and
     // one LDS atomic per wave place each thread's tiles in s.sel[]
@@ -479,12 +494,14 @@ __device__ __forceinline__ void topk_row(const TopkRowArgs& a, int m, TopkSmem& 
         // ---- their logits >= tau (sixteen loads in flight per thread at a time: one round
         // for up to 128 tiles)
         float zv[16];
+        uint32_t mk[16];   // the tile's mask (all groups written without one)
         auto load_round = [&](int base) __attribute__((always_inline)) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int e = base + tid + kThreads * i;
                 const int v = e < nsel * 32 ? s.sel[e >> 5] * 32 + (e & 31) : V;
                 zv[i] = v < V ? row[v] : 0.f;
+                mk[i] = mrow && v < V ? mrow[v >> 5] : 0xFFu;
             }
         };
         auto scan_round = [&](int base) __attribute__((always_inline)) {
@@ -492,7 +509,7 @@ __device__ __forceinline__ void topk_row(const TopkRowArgs& a, int m, TopkSmem& 
             for (int i = 0; i < 16; ++i) {
                 const int e = base + tid + kThreads * i;
                 const int v = e < nsel * 32 ? s.sel[e >> 5] * 32 + (e & 31) : V;
-                if (v < V) {
+                if (v < V && ((mk[i] >> ((v >> 2) & 7)) & 1u)) {
                     const uint32_t k = float_to_key(zv[i]);
                     if (k >= tau) {
                         const int c = atomicAdd(&s.s_ncand, 1);
@@ -518,7 +535,8 @@ __device__ __forceinline__ void topk_row(const TopkRowArgs& a, int m, TopkSmem& 
         }
     }
     // ---- exact path: every chunk of the row, then the merge, all in this workgroup
-    for (int c = 0; c < nchunks; ++c) chunk_select<64>(row, c * (kThreads * 64), V, K, s.lists + (int64_t)c * K, s.sh);
+    for (int c = 0; c < nchunks; ++c)
+        chunk_select<64>(row, c * (kThreads * 64), V, K, s.lists + (int64_t)c * K, s.sh, mrow);
     const uint64_t* fin = merge_lists(s.lists, s.lists + (int64_t)nchunks * K, nchunks, K);
     write_row(fin, m, K, V, lse, d2t, cand_idx, cand_tok, unary);
 }

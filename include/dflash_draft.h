@@ -88,7 +88,18 @@ typedef struct dflash_dims {
     int32_t top_k;         /* K in [1, min(64, V_d)] */
     int32_t rank;          /* r >= 1, table rank */
     int32_t walk;          /* DFLASH_WALK_VITERBI or DFLASH_WALK_GREEDY */
+    int32_t options;       /* 0, or DFLASH_OPT_FILTER_LOGITS */
 } dflash_dims;
+
+/* options: the whole-step calls (dflash_draft_block, dflash_draft_block_sampled) with more
+ * than 64 rows and at least 512 vocabulary tiles of 32 logits never write the fp32 logits
+ * that cannot reach the top K: the exact logits of 128 sampled tiles give each row a bound
+ * (their K-th largest, at most the row's K-th largest logit), the lm_head kernel writes only
+ * the groups of four logits whose maximum reaches it, with a mask of them, and the Top-K reads
+ * only those.  The slots, tokens and scores are those of the unfiltered step, bit for bit.
+ * Off by default: on MI355X the sample costs more than the writes it saves at the Qwen3-4B
+ * and 27B shapes.  Other entry points ignore it. */
+#define DFLASH_OPT_FILTER_LOGITS 1
 
 /* Bytes of workspace every entry point below needs for these dims (the same
  * number for all of them), or 0 with dflash_last_error() set if the dims are

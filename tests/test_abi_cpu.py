@@ -78,6 +78,7 @@ def test_workspace_bytes_and_stride(lib):
     (dict(target_vocab=1000), bdm.EINVAL, "target_vocab"),
     (dict(rank=0), bdm.EINVAL, "rank"),
     (dict(walk=2), bdm.EINVAL, "walk"),
+    (dict(options=2), bdm.EINVAL, "options"),
     (dict(num_requests=-1), bdm.EINVAL, "num_requests"),
     (dict(total_rows=7), bdm.EINVAL, "total_rows"),
     (dict(total_rows=5), bdm.EINVAL, "row_offsets"),   # uniform blocks need M = R * L

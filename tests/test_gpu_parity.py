@@ -353,6 +353,10 @@ def _end_to_end(inp, sample_requests, walk="viterbi", name=None):
     tokens2, scores2 = api_.draft_block(d["hidden"], d["lm_head"], d["tables"], d["last_tok"], top_k=K,
                                         d2t=d["d2t"], gate_w=d["gate_w"], row_offsets=d["row_offsets"],
                                         block_len=L, walk=walk)
+    # the opt-in logits filter (DFLASH_OPT_FILTER_LOGITS): the same tokens and scores bit for bit
+    f_tokens, f_scores = api_.draft_block(d["hidden"], d["lm_head"], d["tables"], d["last_tok"], top_k=K,
+                                          d2t=d["d2t"], gate_w=d["gate_w"], row_offsets=d["row_offsets"],
+                                          block_len=L, walk=walk, filter_logits=True)
     z, lse, idx, tok, un, st_tokens, st_scores, st_slots = _staged(api_, d, inp, K, L, walk)
     lat_tokens, lat_scores = api_.lattice(tok, un, d["tables"], d["last_tok"], gate_w=d["gate_w"],
                                           hidden=d["hidden"], row_offsets=d["row_offsets"], block_len=L, walk=walk)
@@ -363,6 +367,8 @@ def _end_to_end(inp, sample_requests, walk="viterbi", name=None):
     assert np.array_equal(tokens, st_tokens.cpu().numpy())
     assert np.array_equal(scores, st_scores.cpu().numpy())
     assert np.array_equal(tokens, lat_tokens.cpu().numpy()) and np.array_equal(scores, lat_scores.cpu().numpy())
+    assert np.array_equal(tokens, f_tokens.cpu().numpy()) and np.array_equal(scores, f_scores.cpu().numpy()), \
+        "the logits filter changed the step's result"
     idx = idx.cpu().numpy().astype(np.int64)
     gtok = tok.cpu().numpy()
     slots = st_slots.cpu().numpy()
@@ -510,6 +516,36 @@ def test_end_to_end_batched_tile_maxima_paths(name, R, L, V, zero):
     if zero:
         inp = _zero_hidden(inp)
     _end_to_end(inp, list(range(R)))
+
+
+def _scale_rows_bf16(bits, rows, factor):
+    """bf16 rows multiplied by a power of two (exact)."""
+    x = O.bf16_to_f64(bits[rows]) * factor
+    out = bits.copy()
+    out[rows] = di.round_to_bf16_bits(x.astype(np.float32))
+    return out
+
+
+@pytest.mark.parametrize("V", [40003, 151936])
+def test_end_to_end_filter_bound_is_tight(V):
+    """The logits filter (DFLASH_OPT_FILTER_LOGITS; more than 64 rows and at least 512
+    vocabulary tiles; _end_to_end runs the step with and without it): the lm_head writes only the groups
+    of logits that reach a bound from the exact logits of 128 sampled tiles (tile
+    floor(j T / 128), T tiles).  Here the W rows of the sampled tiles are scaled by 8, so
+    every row's top K lies among them and the bound is the row's K-th largest logit itself:
+    a sample logit one rounding above the main kernel's would drop a member of the top K.
+    The filtered step must match the unfiltered stage entry points and the oracle."""
+    sh = di.custom_shape(f"filter_tight_{V}", R=10, L=7, H=128, Vd=V, K=64, r=16, table_std=0.5, seed=90)
+    inp = di.make_inputs(sh)
+    T = (V + 31) // 32
+    tiles = [(j * T) // 128 for j in range(128)]
+    rows = np.concatenate([np.arange(t * 32, t * 32 + 32) for t in tiles])
+    inp.lm_head = _scale_rows_bf16(inp.lm_head, rows, 8.0)
+    z = O.logits(inp.hidden[:3], inp.lm_head)
+    for m in range(3):   # the planted rows do hold each row's top K
+        assert set(O.topk_slots(z[m], 64).tolist()) <= set(rows.tolist())
+    c = _end_to_end(inp, list(range(10)))
+    _assert_mostly_exact(c)
 
 
 def test_empty_batch_is_a_no_op():

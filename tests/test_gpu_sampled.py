@@ -132,6 +132,8 @@ def _sampled_end_to_end(inp, sample_requests, T, seed, name=None):
     kw = dict(top_k=K, temperature=T, d2t=d["d2t"], gate_w=d["gate_w"], row_offsets=d["row_offsets"], block_len=L)
     tokens, scores, q = A.draft_block_sampled(d["hidden"], d["lm_head"], d["tables"], d["last_tok"], Ud, **kw)
     tokens2, scores2, q2 = A.draft_block_sampled(d["hidden"], d["lm_head"], d["tables"], d["last_tok"], Ud, **kw)
+    tokens3, scores3, q3 = A.draft_block_sampled(d["hidden"], d["lm_head"], d["tables"], d["last_tok"], Ud,
+                                                 filter_logits=True, **kw)
     # the staged calls: lm_head, Top-K, pair scores, then the sampled walk
     z, lse = A.lm_head(d["hidden"], d["lm_head"])
     idx, tok, un = A.topk(z, lse, K, d2t=d["d2t"], target_vocab=inp.tables.shape[1])
@@ -142,6 +144,9 @@ def _sampled_end_to_end(inp, sample_requests, T, seed, name=None):
     torch.cuda.synchronize()
     tokens, scores, q = tokens.cpu().numpy(), scores.cpu().numpy(), q.cpu().numpy()
     assert np.array_equal(tokens, tokens2.cpu().numpy()) and np.array_equal(q, q2.cpu().numpy())
+    # the opt-in logits filter: the same draws bit for bit
+    assert np.array_equal(tokens, tokens3.cpu().numpy()) and np.array_equal(q, q3.cpu().numpy())
+    assert np.array_equal(scores, scores3.cpu().numpy())
     assert np.array_equal(tokens, st_tokens.cpu().numpy()) and np.array_equal(scores, st_scores.cpu().numpy())
     assert np.array_equal(q, st_q.cpu().numpy())
     idx, gtok, slots = idx.cpu().numpy().astype(np.int64), tok.cpu().numpy(), st_slots.cpu().numpy()
