@@ -21,6 +21,7 @@
 
 #include "common.hpp"
 #include "internal.hpp"
+#include "lds_dma.hpp"
 
 #include <math.h>
 
@@ -88,40 +89,7 @@ __device__ __forceinline__ void static_for(F&& f) { static_for_impl<0, N>(f); }
 // are in flight while a pass ends with its logits and (max, sum exp)
 // epilogue.  A pass normally gives each wave two tiles; the last pass of a
 // workgroup spreads what is left at one tile per wave when it can.
-__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
-
-constexpr int kBufWord3 = 0x00020000;     // gfx9 buffer descriptor word 3 for raw dword access
 constexpr int kRowsWaves = 4;             // waves, and so (max, sum) partials, per workgroup
-
-typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
-
-constexpr int kBig = 0x40000000;   // buffer offset past every described range (ranges stay < 2^29)
-
-__device__ __forceinline__ constexpr int waitcnt_vm(int n) {
-    // s_waitcnt immediate: vmcnt <= n; expcnt and lgkmcnt unconstrained
-    return (n & 0xf) | (0x7 << 4) | (0xf << 8) | ((n >> 4) << 14);
-}
-
-// Raw buffer descriptor (base, stride 0, size in bytes) in scalar registers.
-__device__ __forceinline__ u32x4 sbuf(const void* base, int64_t bytes) {
-    const uint64_t p = (uint64_t)base;
-    u32x4 r;
-    r[0] = __builtin_amdgcn_readfirstlane((uint32_t)p);
-    r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32) & 0xffffu);
-    r[2] = __builtin_amdgcn_readfirstlane((uint32_t)(bytes < (1 << 29) ? bytes : (1 << 29)));
-    r[3] = kBufWord3;
-    return r;
-}
-
-// buffer_load_dwordx4 ... lds: lane l's 16 bytes at offset voff + soff land at LDS byte lds + 16 l.
-// Issued from inline assembly, so the compiler neither reorders it nor waits for it: every
-// wait for these loads is the explicit s_waitcnt vmcnt in the step loop.
-__device__ __forceinline__ void dma16(u32x4 rsrc, uint32_t lds, int voff, int soff) {
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                 :
-                 : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
-                 : "memory", "m0");
-}
 
 constexpr int kNV = 2;                    // vocab tiles per wave and pass (more than 64 rows)
 constexpr int kWSlots = 3;                // W slots per wave: W runs kWSlots - 1 steps ahead

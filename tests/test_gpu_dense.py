@@ -130,6 +130,14 @@ CASES = [
     ("rank_1", 4, 6, 64, 777, 777, 1, None, 1.0, 0.0, 1.0),
     ("pruned_vocab", 6, 5, 64, 1500, 4000, 16, None, 1.0, 0.0, 0.4),
     ("block_len_100", 2, 100, 64, 1024, 1024, 16, [100, 37], 1.0, 0.0, 0.3),
+    # the LDS-staged kernel at its largest rank (512, the deeper A buffer)
+    ("rank_512_staged", 3, 4, 64, 1500, 1500, 512, None, 1.0, 0.0, 0.05),
+    # ranks the staged kernel does not take: not a multiple of 4 (scalar loads of the
+    # register-streamed kernel), and above 512 (its 16-byte loads, three rank chunks)
+    ("rank_30_register_path", 3, 5, 64, 2003, 2003, 30, None, 1.0, 0.0, 0.2),
+    ("rank_520_register_path", 3, 4, 64, 1500, 1500, 520, None, 1.7, 5.0, 0.05),
+    # 9375 tiles: more than 256 workgroups of at most 32 tiles each
+    ("vocab_300k_wide_grid", 2, 3, 64, 300000, 300000, 16, None, 1.0, 0.0, 0.3),
 ]
 
 
