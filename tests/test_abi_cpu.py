@@ -196,20 +196,21 @@ def test_binding_check_d2t_matches_oracle():
         assert api.check_d2t(d2t, Vd, Vt) == inj
 
 
-def test_m0_only_set_for_lds_dma():
-    """The batched lm_head kernel sets m0 (a register the compiler reserves) in inline
-    assembly right before each buffer_load ... lds.  That is only sound while no
-    compiler-generated code of the kernel relies on m0, which this checks in the
-    gfx950 assembly: every line naming m0 is such a set, and the next line is an
-    LDS-DMA load."""
+@pytest.mark.parametrize("src,kernel", [("lmhead.hip", "lmhead_dma_kernel"), ("dense.hip", "dense_lds_kernel")])
+def test_m0_only_set_for_lds_dma(src, kernel):
+    """The batched lm_head kernel and the LDS-staged dense walk kernel set m0 (a register
+    the compiler reserves) in inline assembly right before each buffer_load ... lds.
+    That is only sound while no compiler-generated code of the kernel relies on m0,
+    which this checks in the gfx950 assembly: every line naming m0 is such a set, and
+    the next line is an LDS-DMA load."""
     import re
     import shutil
     if shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"):
         pytest.skip("hipcc not available")
     from block_draft_markov_amd import build as B
-    text = B.device_asm("lmhead.hip")
-    kernels = re.findall(r"^(_Z\w*lmhead_dma_kernel\w*):", text, re.M)
-    assert kernels, "no batched lm_head kernel in the assembly"
+    text = B.device_asm(src)
+    kernels = re.findall(r"^(_Z\w*" + kernel + r"\w*):", text, re.M)
+    assert kernels, f"no {kernel} in the assembly"
     for name in kernels:
         body = text[text.index(name + ":"):]
         body = body[:body.index(".Lfunc_end")]
