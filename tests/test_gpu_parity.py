@@ -153,6 +153,14 @@ TOPK_CASES = [
     ("many_rows", 224, 151936, 64, "normal"),     # the row count of the 4B batch: the large-chunk plan
     ("long_row", 2, 300000, 64, "normal"),        # 9375 tiles: more than the 8192 tile maxima kept in registers
     ("long_row_ties", 2, 300000, 64, "ints"),     # the same length with heavy ties: the exact path
+    # many rows with ties, zeros, equal logits and short or long rows
+    ("rows128_ties", 130, 9000, 64, "ints"),
+    ("rows128_ragged_v", 128, 70001, 64, "normal"),
+    ("rows128_zeros", 128, 4096, 64, "zeros"),
+    ("rows128_equal", 128, 5000, 64, "equal"),
+    ("rows128_v17", 160, 17, 17, "normal"),
+    ("rows128_v1", 128, 1, 1, "normal"),
+    ("rows128_8192_tiles", 128, 262144, 64, "ints"),   # the most tiles the LDS maxima hold
 ]
 
 
@@ -183,6 +191,14 @@ def test_topk_pruned_d2t_remap():
     sub = np.random.default_rng(5).permutation(Vt)[:Vd]
     d2t = (sub - np.arange(Vd)).astype(np.int64)
     z32 = _make_logits(5, Vd, "normal", 3)
+    _check_topk_exact(z32, 64, d2t, Vt)
+
+
+def test_topk_pruned_d2t_remap_many_rows():
+    Vd, Vt = 114688, 248100
+    sub = np.random.default_rng(6).permutation(Vt)[:Vd]
+    d2t = (sub - np.arange(Vd)).astype(np.int64)
+    z32 = _make_logits(130, Vd, "normal", 4)
     _check_topk_exact(z32, 64, d2t, Vt)
 
 
