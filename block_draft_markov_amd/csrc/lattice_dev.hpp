@@ -29,6 +29,7 @@
 #pragma once
 
 #include "common.hpp"
+#include "lds_dma.hpp"
 #include "../../include/dflash_draft.h"
 
 #include <math.h>
@@ -123,27 +124,69 @@ __device__ __forceinline__ void pair_position(const PairArgs& A, int req, int a,
     const int jt = quad >> 1, kt = quad & 1;
     f32x16 acc = f32x16{};
 
-    // With r % 4 == 0 and 16-byte aligned tables every row is read as float4:
-    // float4 f of a slice is row f / 64 (A rows, then B rows), elements 4 (f % 64) ..
+    // With r % 4 == 0 and 16-byte aligned tables every row is read as float4, and a slice
+    // arrives in four phases of 64 rank elements, two phases in flight at a time: the gather
+    // of later phases runs while the MFMAs of earlier ones do.  Phase h holds groups 8 h ..
+    // 8 h + 7; the first-half waves take groups below gmid and the second-half waves the
+    // rest, each in ascending order, so every wave forms the same sums, in the same order,
+    // as with the whole slice landed first.
     const bool vec = (r & 3) == 0 && (reinterpret_cast<uintptr_t>(A.tables) & 15) == 0;
     for (int i0 = 0; i0 < r; i0 += kRankSlice) {
         const int w = min(kRankSlice, r - i0);        // rank elements of this slice
-        if (vec) {
-            constexpr int kPer = 2 * 64 * kRankSlice / 4 / kPairThreads;   // float4 per thread
-            f32x4 v[kPer];
+        const int w8 = (w + 7) >> 3;                  // elements past w are zero in both operands
+        const int gmid = (w8 + 1) >> 1;
+        const float* arow = &s.As[32 * jt + lr][4 * lh];
+        const float* brow = &s.Bs[32 * kt + lr][4 * lh];
+        auto mfma_groups = [&](int g0, int g1) __attribute__((always_inline)) {
+            for (int gi = g0; gi < g1; ++gi) {
+                const f32x4 av = *reinterpret_cast<const f32x4*>(arow + 8 * gi);
+                const f32x4 bv = *reinterpret_cast<const f32x4*>(brow + 8 * gi);
 #pragma unroll
-            for (int i = 0; i < kPer; ++i) {
-                const int f = tid + i * kPairThreads;       // 0 .. 8191
-                const int b = f >> 12, row = (f >> 6) & 63, c = (f & 63) * 4;
-                const bool ok = row < (b ? K : Jn) && c < w;
-                const float* src = (b ? TB + s.cand_row[row] : TA + s.prev_row[row]) + i0 + c;
-                v[i] = ok ? *reinterpret_cast<const f32x4*>(src) : f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av[e], bv[e], acc, 0, 0, 0);
             }
+        };
+        if (vec) {
+            constexpr int kPhases = 4;
+            constexpr int kPer = 2 * 64 * (kRankSlice / kPhases) / 4 / kPairThreads;   // float4 per thread and phase
+            static_assert(kRankSlice == 256 && kPer == 4, "phases of 64 rank elements");
+            // float4 i of a thread in phase h: operand i / 2 (A, B), row tid / 16 + 32 (i % 2),
+            // elements 64 h + 4 (tid % 16) .. + 3 (16 threads read the 256 contiguous bytes of a
+            // row's phase).  Every load is issued (a row or element past the operand reads the
+            // row's first element and is replaced by zero), so that the waits count loads.
+            const float* rp[kPer];
+            bool rok[kPer];
 #pragma unroll
             for (int i = 0; i < kPer; ++i) {
-                const int f = tid + i * kPairThreads;
-                const int b = f >> 12, row = (f >> 6) & 63, c = (f & 63) * 4;
-                *reinterpret_cast<f32x4*>(b ? &s.Bs[row][c] : &s.As[row][c]) = v[i];
+                const int b = i >> 1, row = (tid >> 4) + 32 * (i & 1);
+                rok[i] = row < (b ? K : Jn);
+                rp[i] = b ? TB + (rok[i] ? s.cand_row[row] : 0) : TA + (rok[i] ? s.prev_row[row] : 0);
+            }
+            f32x4 v[2][kPer];
+            auto load = [&](int h, f32x4 (&dst)[kPer]) __attribute__((always_inline)) {
+                const int c = 64 * h + 4 * (tid & 15);
+#pragma unroll
+                for (int i = 0; i < kPer; ++i)
+                    dst[i] = *reinterpret_cast<const f32x4*>(rp[i] + i0 + (rok[i] && c < w ? c : 0));
+            };
+            load(0, v[0]);
+            __builtin_amdgcn_sched_barrier(0);   // phase 0 issued first, so that its wait leaves phase 1 in flight
+            load(1, v[1]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int h = 0; h < kPhases; ++h) {
+                const int c = 64 * h + 4 * (tid & 15);
+#pragma unroll
+                for (int i = 0; i < kPer; ++i) {
+                    const int b = i >> 1, row = (tid >> 4) + 32 * (i & 1);
+                    const bool ok = rok[i] && c < w;
+                    *reinterpret_cast<f32x4*>(b ? &s.Bs[row][c] : &s.As[row][c]) =
+                        ok ? v[h & 1][i] : f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+                __syncthreads();
+                if (h + 2 < kPhases) load(h + 2, v[h & 1]);
+                __builtin_amdgcn_sched_barrier(0);
+                if (half) mfma_groups(max(8 * h, gmid), min(8 * h + 8, w8));
+                else mfma_groups(8 * h, min(8 * h + 8, gmid));
             }
         } else {
             for (int f = tid; f < 2 * 64 * kRankSlice; f += kPairThreads) {
@@ -152,17 +195,8 @@ __device__ __forceinline__ void pair_position(const PairArgs& A, int req, int a,
                 const float v = ok ? (b ? TB[s.cand_row[row] + i0 + c] : TA[s.prev_row[row] + i0 + c]) : 0.f;
                 if (b) s.Bs[row][c] = v; else s.As[row][c] = v;
             }
-        }
-        __syncthreads();
-        const int w8 = (w + 7) >> 3;                  // elements past w are zero in both operands
-        const int gmid = (w8 + 1) >> 1;
-        const float* arow = &s.As[32 * jt + lr][4 * lh];
-        const float* brow = &s.Bs[32 * kt + lr][4 * lh];
-        for (int gi = half ? gmid : 0; gi < (half ? w8 : gmid); ++gi) {
-            const f32x4 av = *reinterpret_cast<const f32x4*>(arow + 8 * gi);
-            const f32x4 bv = *reinterpret_cast<const f32x4*>(brow + 8 * gi);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av[e], bv[e], acc, 0, 0, 0);
+            __syncthreads();
+            if (half) mfma_groups(gmid, w8); else mfma_groups(0, gmid);
         }
         __syncthreads();
     }
@@ -209,7 +243,6 @@ struct WalkSmem {
     float qbest[2][4][64];
     int qarg[2][4][64];
     uint8_t back[DFLASH_MAX_BLOCK_LEN][64];
-    __attribute__((aligned(16))) float dsh[4][64];   // delta of the previous position, one row per wave
     int path[DFLASH_MAX_BLOCK_LEN];
     float s_score;
 };
@@ -237,12 +270,14 @@ __device__ __forceinline__ void walk_request(const WalkArgs& A, int req, WalkSme
     auto load_chunk = [&](int c0) {
         const int cn = min(kWalkChunk, n - c0);
         const f32x4* src = reinterpret_cast<const f32x4*>(A.pair + (int64_t)(a + c0) * KK);
+        // u first: whatever wait its register needs then covers no load of S
+        uv = tid < cn * K ? A.unary[(int64_t)(a + c0) * K + tid] : 0.f;
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < kWalkChunk * 4; ++i) {
             const int e = tid + i * kLatThreads;
             if (e < cn * 1024) sv[i] = src[e];
         }
-        uv = tid < cn * K ? A.unary[(int64_t)(a + c0) * K + tid] : 0.f;
     };
     auto store_chunk = [&](int c0, int buf) {
         const int cn = min(kWalkChunk, n - c0);
@@ -252,6 +287,9 @@ __device__ __forceinline__ void walk_request(const WalkArgs& A, int req, WalkSme
             if (e < cn * 1024) reinterpret_cast<f32x4*>(&s.Ss[buf][0][0])[e] = sv[i];
         }
         if (tid < cn * K) s.Us[buf][tid / K][tid % K] = uv;
+        // every load of the chunk has landed, on every path through the stores above, so the
+        // loads of the next chunk need not wait for these registers
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     };
     auto stage_generic = [&](int c0, int buf) {
         const int cn = min(kWalkChunk, n - c0);
@@ -283,24 +321,19 @@ __device__ __forceinline__ void walk_request(const WalkArgs& A, int req, WalkSme
                 if (p == 0) {
                     d = act ? s.Us[buf][0][lane] + s.Ss[buf][0][lane] : -INFINITY;
                 } else {
-                    // the 16 S entries of this quarter and the 16 delta(j) first (independent
-                    // LDS reads and readlanes), then a tree over (value, j) in which the
-                    // higher j wins only by strict >: the lowest j reaching the maximum, as an
-                    // ascending scan with strict > (slots past K are -inf)
-                    float svq[16], vv[16];
+                    // the 16 S entries of this quarter and u first (LDS reads that do not
+                    // depend on delta), delta(j) of the quarter by readlane (every wave holds
+                    // the same delta, lane k holding delta(k)), then a tree over (value, j) in
+                    // which the higher j wins only by strict >: the lowest j reaching the
+                    // maximum, as an ascending scan with strict > (slots past K are -inf)
+                    float svq[16], vv[16], dq[16];
                     int jj[16];
-                    // delta(j) of the quarter reaches every lane through the wave's own LDS row
-                    // (one write, four broadcast reads): in-order LDS access within a wave
-                    // needs no barrier
-                    s.dsh[q][lane] = d;
 #pragma unroll
                     for (int t = 0; t < 16; ++t) svq[t] = s.Ss[buf][pp][(16 * q + t) * 64 + lane];
-                    const f32x4* drow = reinterpret_cast<const f32x4*>(&s.dsh[q][16 * q]);
-                    const f32x4 d0 = drow[0], d1 = drow[1], d2 = drow[2], d3 = drow[3];
-                    // every LDS read above is issued before the first sum below uses one
-                    __builtin_amdgcn_sched_barrier(0);
-                    const float dq[16] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3],
-                                          d2[0], d2[1], d2[2], d2[3], d3[0], d3[1], d3[2], d3[3]};
+                    const float us = s.Us[buf][pp][lane];
+#pragma unroll
+                    for (int t = 0; t < 16; ++t)
+                        dq[t] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(d), 16 * q + t));
 #pragma unroll
                     for (int t = 0; t < 16; ++t) {
                         const int j = 16 * q + t;
@@ -323,7 +356,7 @@ __device__ __forceinline__ void walk_request(const WalkArgs& A, int req, WalkSme
                     for (int qq = 1; qq < 4; ++qq)
                         if (s.qbest[par][qq][lane] > bb) { bb = s.qbest[par][qq][lane]; ar = s.qarg[par][qq][lane]; }
                     if (bb == -INFINITY) ar = 0;   // nothing finite to extend: slot 0, as a scan from j = 0
-                    d = act ? s.Us[buf][pp][lane] + bb : -INFINITY;
+                    d = act ? us + bb : -INFINITY;
                     if (q == 0) s.back[p][lane] = (uint8_t)min(ar, K - 1);
                     par ^= 1;
                 }
