@@ -45,6 +45,7 @@ constexpr int kRankSlice = 256;     // rank elements staged per round
 constexpr int kPitch = kRankSlice + 4;   // LDS row pitch (floats): 16 consecutive rows hit distinct banks
 constexpr int kWalkSampled = 2;     // the sampled walk (its own entry points; not a dims.walk value)
 constexpr int kWalkChunk = 4;       // positions of S and u per LDS buffer; two buffers
+constexpr int kRegPositions = 16;   // Viterbi blocks of at most this many positions keep S in registers
 
 // Rows of request req: [a, a + n), n at most L (uniform blocks of L rows without offsets).
 __device__ __forceinline__ void row_range(const int32_t* row_offsets, int req, int L, int M, int& a, int& n) {
@@ -247,6 +248,111 @@ struct WalkSmem {
     float s_score;
 };
 
+// One Viterbi position p >= 1 by the four waves: wave q takes the best delta(j) + S[j][k]
+// over its quarter j in [16 q, 16 q + 16) (svq[t] = S[16 q + t][k] in lane k, u = u_p[k]),
+// then after one barrier the four quarters are combined in order (strict >), so the lowest
+// j reaching the maximum wins; delta is updated in place and lane k's back-pointer returned.
+// Every wave holds the same delta, lane k holding delta(k), and reads delta(j) by readlane.
+__device__ __forceinline__ int viterbi_position(const float (&svq)[16], float us, int K, int q, int lane, float& d,
+                                                int& par, WalkSmem& s) {
+    const bool act = lane < K;
+    float vv[16], dq[16];
+    int jj[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) dq[t] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(d), 16 * q + t));
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+        const int j = 16 * q + t;
+        vv[t] = j < K ? dq[t] + svq[t] : -INFINITY;
+        jj[t] = j;
+    }
+    // a tree over (value, j) in which the higher j wins only by strict >: the lowest j
+    // reaching the maximum, as an ascending scan with strict > (slots past K are -inf)
+#pragma unroll
+    for (int w = 1; w < 16; w *= 2)
+#pragma unroll
+        for (int t = 0; t < 16; t += 2 * w)
+            if (vv[t + w] > vv[t]) { vv[t] = vv[t + w]; jj[t] = jj[t + w]; }
+    s.qbest[par][q][lane] = vv[0];
+    s.qarg[par][q][lane] = jj[0];
+    __syncthreads();
+    float bb = s.qbest[par][0][lane];
+    int ar = s.qarg[par][0][lane];
+#pragma unroll
+    for (int qq = 1; qq < 4; ++qq)
+        if (s.qbest[par][qq][lane] > bb) { bb = s.qbest[par][qq][lane]; ar = s.qarg[par][qq][lane]; }
+    if (bb == -INFINITY) ar = 0;   // nothing finite to extend: slot 0, as a scan from j = 0
+    d = act ? us + bb : -INFINITY;
+    par ^= 1;
+    return min(ar, K - 1);
+}
+
+// The Viterbi walk of a block of at most NP positions with S, u, the candidates' target ids
+// and the back-pointers in registers instead of LDS: lane k of wave q holds S_p[16 q + t][k]
+// (t < 16), u_p[k] and the id of slot k of every position; the loads of position p + kAhead
+// are issued as position p starts (at most 63 loads in flight per wave), so each position
+// waits only for its own loads.  Clamped indices keep every load inside the request's rows;
+// lanes and rows past K are masked.  The back-tracking reads the back-pointers by readlane
+// (every wave holds the same ones); wave 0 writes tokens, slots and the score.
+template <int NP>
+__device__ __forceinline__ void viterbi_in_registers(const WalkArgs& A, int req, int a, int n, int q, int lane,
+                                                     WalkSmem& s) {
+    constexpr int kAhead = 3;   // 17 loads per position: three positions ahead stay under 63
+    const int K = A.K, KK = K * K;
+    const bool act = lane < K;
+    const int kc = act ? lane : K - 1;
+    // a wave-uniform base and 32-bit byte offsets: one address register per load
+    auto at = [](const float* base, uint32_t i) __attribute__((always_inline)) {
+        return *reinterpret_cast<const float*>(reinterpret_cast<const char*>(base) + (i << 2));
+    };
+    int64_t ct[NP];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) ct[p] = A.cand_tok[(int64_t)(a + (p < n ? p : n - 1)) * K + kc];
+    float sv[NP][16], uv[NP];
+    auto load = [&](int p) __attribute__((always_inline)) {
+        const int pc = p < n ? p : n - 1;
+        const float* Sp = A.pair + (int64_t)(a + pc) * KK;
+        uv[p] = at(A.unary + (int64_t)(a + pc) * K, (uint32_t)kc);
+#pragma unroll
+        for (int t = 0; t < 16; ++t) sv[p][t] = at(Sp, (uint32_t)(min(16 * q + t, K - 1) * K + kc));
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    const float s0 = A.pair[(int64_t)a * KK + kc];   // S_0[0][k]: the row of the token before the block
+    uv[0] = A.unary[(int64_t)a * K + kc];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int p = 1; p <= kAhead && p < NP; ++p) load(p);
+    float d = act ? uv[0] + s0 : -INFINITY;
+    int par = 0;
+    int bk[NP];
+#pragma unroll
+    for (int p = 1; p < NP; ++p) {
+        if (p + kAhead < NP) load(p + kAhead);
+        bk[p] = p < n ? viterbi_position(sv[p], uv[p], K, q, lane, d, par, s) : 0;
+    }
+    const float score = wave_max(d);
+    // NaN scores match no lane: fall back to slot 0 rather than index past the slots
+    int c = min(lowest_lane(act && d == score), K - 1);
+    int64_t tok = 0;
+    int slot = 0;
+#pragma unroll
+    for (int p = NP - 1; p >= 0; --p) {
+        if (p < n) {
+            const int64_t t = ((int64_t)__builtin_amdgcn_readlane((int)(ct[p] >> 32), c) << 32) |
+                              (uint32_t)__builtin_amdgcn_readlane((int)ct[p], c);
+            if (lane == p) { tok = t; slot = c; }
+            if (p > 0) c = __builtin_amdgcn_readlane(bk[p], c);
+        }
+    }
+    if (q == 0) {
+        if (lane == 0) A.scores[req] = score;
+        if (lane < n) {
+            A.tokens[a + lane] = tok;
+            if (A.slots) A.slots[a + lane] = slot;
+        }
+    }
+}
+
 // The walk of request req through its lattice; writes tokens, scores (and slots, q).
 __device__ __forceinline__ void walk_request(const WalkArgs& A, int req, WalkSmem& s) {
     const int tid = threadIdx.x;
@@ -301,16 +407,21 @@ __device__ __forceinline__ void walk_request(const WalkArgs& A, int req, WalkSme
         for (int e = tid; e < cn * K; e += kLatThreads) s.Us[buf][e / K][e % K] = A.unary[(int64_t)(a + c0) * K + e];
     };
 
-    if (vec) { load_chunk(0); store_chunk(0, 0); } else { stage_generic(0, 0); }
-    __syncthreads();
-
-    // Viterbi: every wave keeps delta of the previous position in lane k (d), reads
-    // delta(j) by readlane, takes the best over its quarter j in [16 q, 16 q + 16),
-    // and after one barrier combines the four quarters in order (strict >).
+    // Viterbi: every wave keeps delta of the previous position in lane k (d); a block of at
+    // most kRegPositions positions keeps S and u in registers, a longer one (and the other
+    // walks) stages kWalkChunk positions at a time in LDS
     float d = -INFINITY;
     int prev = 0;            // greedy: slot of the previous position (wave 0)
     float total = 0.f;       // greedy: running score (wave 0)
     int par = 0;             // parity of the qbest buffers
+    if (walk == DFLASH_WALK_VITERBI && n <= kRegPositions) {
+        if (n <= kRegPositions / 2) viterbi_in_registers<kRegPositions / 2>(A, req, a, n, q, lane, s);
+        else viterbi_in_registers<kRegPositions>(A, req, a, n, q, lane, s);
+        return;
+    }
+    {
+    if (vec) { load_chunk(0); store_chunk(0, 0); } else { stage_generic(0, 0); }
+    __syncthreads();
     for (int c0 = 0, buf = 0; c0 < n; c0 += kWalkChunk, buf ^= 1) {
         const int cn = min(kWalkChunk, n - c0);
         const bool more = c0 + kWalkChunk < n;
@@ -321,44 +432,13 @@ __device__ __forceinline__ void walk_request(const WalkArgs& A, int req, WalkSme
                 if (p == 0) {
                     d = act ? s.Us[buf][0][lane] + s.Ss[buf][0][lane] : -INFINITY;
                 } else {
-                    // the 16 S entries of this quarter and u first (LDS reads that do not
-                    // depend on delta), delta(j) of the quarter by readlane (every wave holds
-                    // the same delta, lane k holding delta(k)), then a tree over (value, j) in
-                    // which the higher j wins only by strict >: the lowest j reaching the
-                    // maximum, as an ascending scan with strict > (slots past K are -inf)
-                    float svq[16], vv[16], dq[16];
-                    int jj[16];
+                    // the 16 S entries of this quarter and u first (LDS reads that do not depend
+                    // on delta)
+                    float svq[16];
 #pragma unroll
                     for (int t = 0; t < 16; ++t) svq[t] = s.Ss[buf][pp][(16 * q + t) * 64 + lane];
-                    const float us = s.Us[buf][pp][lane];
-#pragma unroll
-                    for (int t = 0; t < 16; ++t)
-                        dq[t] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(d), 16 * q + t));
-#pragma unroll
-                    for (int t = 0; t < 16; ++t) {
-                        const int j = 16 * q + t;
-                        vv[t] = j < K ? dq[t] + svq[t] : -INFINITY;
-                        jj[t] = j;
-                    }
-#pragma unroll
-                    for (int w = 1; w < 16; w *= 2)
-#pragma unroll
-                        for (int t = 0; t < 16; t += 2 * w)
-                            if (vv[t + w] > vv[t]) { vv[t] = vv[t + w]; jj[t] = jj[t + w]; }
-                    const float best = vv[0];
-                    const int arg = jj[0];
-                    s.qbest[par][q][lane] = best;
-                    s.qarg[par][q][lane] = arg;
-                    __syncthreads();
-                    float bb = s.qbest[par][0][lane];
-                    int ar = s.qarg[par][0][lane];
-#pragma unroll
-                    for (int qq = 1; qq < 4; ++qq)
-                        if (s.qbest[par][qq][lane] > bb) { bb = s.qbest[par][qq][lane]; ar = s.qarg[par][qq][lane]; }
-                    if (bb == -INFINITY) ar = 0;   // nothing finite to extend: slot 0, as a scan from j = 0
-                    d = act ? us + bb : -INFINITY;
-                    if (q == 0) s.back[p][lane] = (uint8_t)min(ar, K - 1);
-                    par ^= 1;
+                    const int bp = viterbi_position(svq, s.Us[buf][pp][lane], K, q, lane, d, par, s);
+                    if (q == 0) s.back[p][lane] = (uint8_t)bp;
                 }
             } else if (walk == kWalkSampled) {
                 if (tid < 64) {
@@ -398,6 +478,7 @@ __device__ __forceinline__ void walk_request(const WalkArgs& A, int req, WalkSme
             if (vec) store_chunk(c0 + kWalkChunk, buf ^ 1); else stage_generic(c0 + kWalkChunk, buf ^ 1);
             __syncthreads();
         }
+    }
     }
     if (tid < 64) {
         float score;

@@ -321,6 +321,11 @@ WALK_CASES = [
     ("ragged_with_empty", [3, 0, 9, 1, 0], 16, "normal"),
     ("exact_ties", [6] * 20, 4, "ints"),         # small integers: exact ties in fp32 and fp64
     ("exact_ties_k64", [7] * 8, 64, "ints"),
+    # Viterbi blocks of up to 8 and up to 16 positions keep S in registers, longer ones stage it in LDS
+    ("l8_k33", [8, 2, 8, 5], 33, "normal"),
+    ("l8_and_l9", [8, 9, 8, 9], 64, "normal"),
+    ("l16_and_l17", [16, 17, 3, 16], 64, "normal"),
+    ("l16_k20", [16, 11, 16], 20, "normal"),
 ]
 
 
