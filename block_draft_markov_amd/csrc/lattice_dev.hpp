@@ -40,7 +40,7 @@ namespace {
 
 constexpr int kLatThreads = 256;    // threads of a walk workgroup: four waves
 constexpr int kPairThreads = 512;   // threads of a scorer workgroup: eight waves
-constexpr int kGateThreads = 256;   // threads of the gate's dot product
+constexpr int kGateRounds = 2;      // gate: rounds of 8 elements per thread whose loads are all issued first
 constexpr int kRankSlice = 256;     // rank elements staged per round
 constexpr int kPitch = kRankSlice + 4;   // LDS row pitch (floats): 16 consecutive rows hit distinct banks
 constexpr int kWalkSampled = 2;     // the sampled walk (its own entry points; not a dims.walk value)
@@ -80,7 +80,7 @@ struct PairSmem {
     __attribute__((aligned(16))) float As[64][kPitch];
     __attribute__((aligned(16))) float Bs[64][kPitch];
     int64_t prev_row[64], cand_row[64];
-    float red[4];
+    float red[kPairThreads / 64];
 };
 
 // S of position p of request req, whose rows start at row a (row m = a + p), into pair[m];
@@ -97,17 +97,46 @@ __device__ __forceinline__ void pair_position(const PairArgs& A, int req, int a,
         const int64_t cand = tid < K ? A.cand_tok[(int64_t)m * K + tid] : 0;
         s.cand_row[tid] = clamp_tok(cand, Vt) * r;
     }
-    if (A.gate_w && tid < kGateThreads) {
-        float part = 0.f;
+    if (A.gate_w) {
+        // w . h_p: eight consecutive elements per thread and round, the loads of every round
+        // issued before the first product (one round trip for H up to 8192), then a fixed
+        // tree over the lanes and the waves
         const uint16_t* h = A.hidden + (int64_t)m * H;
-        for (int i = tid; i < H; i += kGateThreads) part += A.gate_w[i] * bf16_bits_to_float(h[i]);
+        float part = 0.f;
+        if ((H & 7) == 0 && (reinterpret_cast<uintptr_t>(A.gate_w) & 15) == 0 &&
+            (reinterpret_cast<uintptr_t>(h) & 15) == 0) {
+            for (int base = 0; base < H; base += 8 * kPairThreads * kGateRounds) {
+                u32x4 hv[kGateRounds];
+                f32x4 ga[kGateRounds], gb[kGateRounds];
+#pragma unroll
+                for (int u = 0; u < kGateRounds; ++u) {
+                    const int i = base + 8 * (tid + u * kPairThreads);
+                    const bool ok = i < H;
+                    hv[u] = ok ? *reinterpret_cast<const u32x4*>(h + i) : u32x4{0u, 0u, 0u, 0u};
+                    ga[u] = ok ? *reinterpret_cast<const f32x4*>(A.gate_w + i) : f32x4{0.f, 0.f, 0.f, 0.f};
+                    gb[u] = ok ? *reinterpret_cast<const f32x4*>(A.gate_w + i + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+#pragma unroll
+                for (int u = 0; u < kGateRounds; ++u) {
+                    const float wv[8] = {ga[u][0], ga[u][1], ga[u][2], ga[u][3], gb[u][0], gb[u][1], gb[u][2], gb[u][3]};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {   // a dword holds elements 2 e (low half) and 2 e + 1
+                        part += wv[2 * e] * __uint_as_float(hv[u][e] << 16);
+                        part += wv[2 * e + 1] * __uint_as_float(hv[u][e] & 0xFFFF0000u);
+                    }
+                }
+            }
+        } else {
+            for (int i = tid; i < H; i += kPairThreads) part += A.gate_w[i] * bf16_bits_to_float(h[i]);
+        }
         part = wave_sum(part);
         if ((tid & 63) == 0) s.red[tid >> 6] = part;
     }
     __syncthreads();
     float g = 1.f;
     if (A.gate_w) {
-        const float x = (s.red[0] + s.red[1]) + (s.red[2] + s.red[3]);
+        static_assert(kPairThreads == 512, "eight wave sums");
+        const float x = ((s.red[0] + s.red[1]) + (s.red[2] + s.red[3])) + ((s.red[4] + s.red[5]) + (s.red[6] + s.red[7]));
         g = 1.f / (1.f + expf(-x));
     }
 
