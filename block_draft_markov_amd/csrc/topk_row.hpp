@@ -98,21 +98,17 @@ __device__ __forceinline__ void rank_place(const uint64_t* list, int n, int K, u
     for (int i = n + threadIdx.x; i < K; i += kThreads) out[i] = kEmptyEntry;
 }
 
-// The 64 lanes' values sorted in descending order across the wave (bitonic
-// network over lane pairs); lane i returns the (i+1)-th largest.
-__device__ __forceinline__ uint32_t wave_sort_desc(uint32_t x) {
-    const int lane = threadIdx.x & 63;
+// The q-th largest (1 <= q <= 64) of the 64 lanes' values, in every lane: the largest t with at
+// least q lanes >= t, built bit by bit from the top (one ballot and one population count per
+// bit, no exchange through LDS).  Every lane of the wave calls it.
+__device__ __forceinline__ uint32_t wave_kth_largest(uint32_t x, int q) {
+    uint32_t t = 0;
 #pragma unroll
-    for (int k = 2; k <= 64; k <<= 1) {
-#pragma unroll
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            const uint32_t y = (uint32_t)__shfl_xor((int)x, j);
-            const bool desc = (lane & k) == 0;
-            const bool lower = (lane & j) == 0;
-            x = (desc == lower) ? max(x, y) : min(x, y);
-        }
+    for (int b = 31; b >= 0; --b) {
+        const uint32_t c = t | (1u << b);
+        if (__popcll(__ballot(x >= c)) >= q) t = c;
     }
-    return x;
+    return t;
 }
 
 struct ChunkShared {
@@ -154,9 +150,8 @@ __device__ __forceinline__ void chunk_select(const float* __restrict__ row, int 
     uint32_t mx = 0;
 #pragma unroll
     for (int e = 0; e < PT; ++e) mx = max(mx, key[e]);
-    const uint32_t sorted = wave_sort_desc(mx);
     const int q = (K + 3) >> 2;
-    const uint32_t wq = (uint32_t)__builtin_amdgcn_readlane((int)sorted, q - 1);
+    const uint32_t wq = wave_kth_largest(mx, q);
     if ((tid & 63) == 0) sh.wtau[tid >> 6] = wq;
     __syncthreads();
     const uint32_t tau = max(min(min(sh.wtau[0], sh.wtau[1]), min(sh.wtau[2], sh.wtau[3])), 1u);   // key 0: past the row
@@ -442,9 +437,8 @@ __device__ __forceinline__ void topk_row(const TopkRowArgs& a, int m, TopkSmem& 
         mx = max(mx, kv[i]);
     }
     for (int t = kTileCap + tid; t < tiles; t += kThreads) mx = max(mx, float_to_key(trow[t]));
-    const uint32_t sorted = wave_sort_desc(mx);
     const int q = (K + 3) >> 2;
-    const uint32_t wq = (uint32_t)__builtin_amdgcn_readlane((int)sorted, q - 1);
+    const uint32_t wq = wave_kth_largest(mx, q);
     if ((tid & 63) == 0) s.sh.wtau[tid >> 6] = wq;
     if (tid == 0) { s.s_nsel = 0; s.s_ncand = 0; }
     __syncthreads();
