@@ -248,6 +248,34 @@ def test_pair_scores_parity(name, R, L, K, r, gated, ragged):
                 assert np.all(pair[a, 1:, :] == 0.0)
 
 
+@pytest.mark.parametrize("H,aligned", [(8, False), (64, False), (5120, True), (9000, True)])
+def test_pair_scores_gate_hidden_sizes(H, aligned):
+    """The gate w . h_p: a gate vector that is not 16-byte aligned (element loop), one round
+    of 16-byte loads (5120) and more than one (9000)."""
+    say(f"pair gate H={H} aligned={aligned}")
+    rng = np.random.default_rng(H)
+    R, L, K, r, Vt = 2, 3, 16, 64, 500
+    M = R * L
+    off = di.ragged_offsets([L] * R)
+    tok = rng.integers(0, Vt, size=(M, K)).astype(np.int64)
+    tables = f32(rng.standard_normal((2, Vt, r)) * 0.25)
+    hidden = di.round_to_bf16_bits(f32(rng.standard_normal((M, H))))
+    w = f32(rng.standard_normal(H) / np.sqrt(H))
+    last = rng.integers(0, Vt, size=R).astype(np.int64)
+    wd = dev(w) if aligned else dev(np.concatenate([np.zeros(1, np.float32), w]))[1:]   # 4 bytes past 16
+    assert (wd.data_ptr() % 16 == 0) == aligned
+    pair = api().pair_scores(dev(tok), dev(tables), dev(last), gate_w=wd, hidden=dev_bf16(hidden), block_len=L)
+    pair = pair.cpu().numpy().astype(np.float64)
+    h64 = O.bf16_to_f64(hidden)
+    for req in range(R):
+        a = int(off[req])
+        S = O.lattice_scores(tok[a:a + L], tables, h64[a:a + L], w, int(last[req]))
+        for p, s in enumerate(S):
+            got = pair[a + p, :1, :] if p == 0 else pair[a + p]
+            scale = max(1.0, float(np.max(np.abs(s))))
+            assert np.max(np.abs(got - s)) <= 1e-5 * scale, f"request {req} position {p}"
+
+
 # ============================================================ part 4: walk
 
 def _walk_fed(u64, S_all, off, R, K, walk, L):
