@@ -10,17 +10,18 @@
 //   S_p[j][k] = g_p * <A[t_{p-1}[j]], B[t_p[k]]>,  S_0[0][k] = g_0 * <A[last], B[t_0[k]]>,
 //   g_p = sigmoid(w . h_p) when gated, else 1.
 // One workgroup per (position, request).  The K rows of A and of B it needs
-// are gathered whole (up to 256 rank elements at a time), every load in flight
-// at once, into LDS rows of 260 floats (the 32 rows a wave reads fall in
-// distinct banks); eight waves compute S with fp32 MFMAs, two per 32 x 32
-// quadrant, each over one half of the rank.
+// are gathered 256 rank elements at a time, in four phases with two in flight,
+// into LDS rows of 260 floats (the 32 rows a wave reads fall in distinct
+// banks); eight waves compute S with fp32 MFMAs, two per 32 x 32 quadrant, each
+// over one half of the rank, starting as soon as their phases have landed.
 //
 // Walk (same commit: the greedy walk takes the best candidate after the token
 // before; the max-score walk is its Viterbi form): one 256-thread workgroup per
-// request stages up to eight positions of S and u in LDS at a time.  Viterbi:
-// thread (k, q) takes the best delta(j) + S[j][k] over j in its quarter q of
-// the slots (ascending, strict >), and the quarters are combined in order, so
-// the lowest j wins a tie; back-pointers stay in LDS.  Greedy: one wave, an
+// request.  Viterbi: thread (k, q) takes the best delta(j) + S[j][k] over j in
+// its quarter q of the slots (ascending, strict >), and the quarters are
+// combined in order, so the lowest j wins a tie; a block of at most 16
+// positions keeps S, u and the back-pointers in registers, a longer one stages
+// four positions of S and u at a time in two LDS buffers.  Greedy: one wave, an
 // argmax per position (DPP max reduction, lowest lane of a ballot).  Sampled
 // (same commit: a sampled request walks the lattice with its draft RNG; the
 // sampled-drafting commits: float weights, double sums, a double uniform, the
@@ -448,7 +449,6 @@ __device__ __forceinline__ void walk_request(const WalkArgs& A, int req, WalkSme
         else viterbi_in_registers<kRegPositions>(A, req, a, n, q, lane, s);
         return;
     }
-    {
     if (vec) { load_chunk(0); store_chunk(0, 0); } else { stage_generic(0, 0); }
     __syncthreads();
     for (int c0 = 0, buf = 0; c0 < n; c0 += kWalkChunk, buf ^= 1) {
@@ -507,7 +507,6 @@ __device__ __forceinline__ void walk_request(const WalkArgs& A, int req, WalkSme
             if (vec) store_chunk(c0 + kWalkChunk, buf ^ 1); else stage_generic(c0 + kWalkChunk, buf ^ 1);
             __syncthreads();
         }
-    }
     }
     if (tid < 64) {
         float score;
