@@ -217,6 +217,9 @@ PAIR_CASES = [
     ("gated", 2, 15, 64, 256, True, None),
     ("k5_r100", 3, 4, 5, 100, True, None),     # K % 4 != 0, rank not a multiple of the 64-wide slice
     ("ragged", 4, 6, 16, 32, False, [3, 0, 6, 1]),
+    ("r30_elementwise", 2, 5, 64, 30, True, None),   # rank not a multiple of 4: the element-wise gather
+    ("r260_two_slices", 2, 4, 64, 260, False, None),  # a full 256-element slice, then 4 elements
+    ("r520_three_slices", 1, 3, 33, 520, True, None),
 ]
 
 
